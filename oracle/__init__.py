@@ -1,0 +1,221 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``exact_attention_77_amd``) and neither imports the other.
+
+The numerics live in ``oracle.c`` (plain two-pass fp64 attention, its analytic
+gradient, an OCP e4m3 codec, a dense Hadamard rotation and block quantisation);
+this module compiles it with gcc on first use and wraps it with ctypes over
+numpy arrays.  See ``oracle.c`` for the passages each function follows:
+"FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析" sec. 2.1, 6.1,
+7.2, 11.3 and "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+Low-precision" sec. 技術 3 / 数値誤差.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+closed forms, invariants, brute force in 50-digit arithmetic (mpmath) and
+library routines (torch fp64 SDPA, torch.float8_e4m3fn, scipy's Hadamard).
+The fp8 P-quantisation rule (``p_quant=1``) is a reading of a silent point; its
+arithmetic is pinned by the codec tests, its choice is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test of the pins themselves may point the wrapper at a deliberately broken
+# build of oracle.c (see tests/test_oracle_mutants.py); nothing else sets this.
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB_OVERRIDE")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2 -fopenmp)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if _LIB_OVERRIDE:
+                lib = ctypes.CDLL(_LIB_OVERRIDE)
+            else:
+                build()
+                lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I = ctypes.c_int64
+            lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_attn_fwd_rows.argtypes = [P, P, P, I, I, I, I, ctypes.c_int,
+                                                 ctypes.c_double, ctypes.c_int, P, I, P, P]
+            lib.oracle_attn_probs_row.argtypes = [P, P, I, I, I, I, ctypes.c_int,
+                                                  ctypes.c_double, I, P]
+            lib.oracle_attn_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int,
+                                                 ctypes.c_double, P, I, P, I, P, P, P]
+            lib.oracle_e4m3_encode.argtypes = [P, I, P]
+            lib.oracle_e4m3_decode.argtypes = [P, I, P]
+            lib.oracle_rotate_rows.argtypes = [P, I, I, P, P]
+            lib.oracle_quantize_blocks.argtypes = [P, I, I, I, I, P, P]
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().oracle_num_threads())
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
+             rows=None, p_quant: bool = False):
+    """Exact attention O = softmax(scale*QK^T) V and LSE = m + ln(l), fp64.
+
+    q, k, v: [B, H, N, d] (any float dtype; upcast to fp64 exactly).
+    rows: None for every row, else flat row ids (b*H + h)*N + i.
+    Returns (o, lse): o is [B, H, N, d] / [len(rows), d], lse [B, H, N] / [len(rows)].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lib = _load()
+    if rows is None:
+        o = np.empty((B, H, N, d), np.float64)
+        lse = np.empty((B, H, N), np.float64)
+        lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, int(causal),
+                                 float(scale), int(p_quant), None, 0, _ptr(o), _ptr(lse))
+        return o, lse
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert r.ndim == 1 and (r.size == 0 or (r.min() >= 0 and r.max() < B * H * N))
+    o = np.empty((r.size, d), np.float64)
+    lse = np.empty((r.size,), np.float64)
+    if r.size:
+        lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, int(causal),
+                                 float(scale), int(p_quant), _ptr(r), r.size, _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def attn_probs_row(q, k, flat_row: int, causal: bool = False, scale: float | None = None):
+    """Row P[i, :] of the probability matrix of one (b, h); zeros where masked."""
+    q, k = _f64(q), _f64(k)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    p = np.empty((N,), np.float64)
+    _load().oracle_attn_probs_row(_ptr(q), _ptr(k), B, H, N, d, int(causal), float(scale),
+                                  int(flat_row), _ptr(p))
+    return p
+
+
+def attn_bwd(q, k, v, dout, causal: bool = False, scale: float | None = None,
+             qrows=None, krows=None):
+    """Analytic gradient (dQ, dK, dV) of the exact-attention definition, fp64.
+
+    With qrows/krows None every row is returned as [B, H, N, d]; otherwise the
+    selected rows as [len(rows), d].
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lib = _load()
+    full = qrows is None and krows is None
+    if full:
+        dq = np.empty((B, H, N, d)); dk = np.empty((B, H, N, d)); dv = np.empty((B, H, N, d))
+        lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, int(causal),
+                                 float(scale), None, 0, None, 0, _ptr(dq), _ptr(dk), _ptr(dv))
+        return dq, dk, dv
+    qr = np.ascontiguousarray(np.asarray([] if qrows is None else qrows, dtype=np.int64))
+    kr = np.ascontiguousarray(np.asarray([] if krows is None else krows, dtype=np.int64))
+    dq = np.empty((max(qr.size, 1), d)); dk = np.empty((max(kr.size, 1), d)); dv = np.empty((max(kr.size, 1), d))
+    lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, int(causal),
+                             float(scale), _ptr(qr), qr.size, _ptr(kr), kr.size,
+                             _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq[:qr.size], dk[:kr.size], dv[:kr.size]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """OCP e4m3fn codes (uint8) of x: RNE, saturating at +-448, NaN -> 0x7F."""
+    x = _f64(x)
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_e4m3_encode(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (fp64) of OCP e4m3fn codes."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_decode(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def rotate(x, signs) -> np.ndarray:
+    """Incoherent processing x -> (x * signs) H_d / sqrt(d), dense, along the last axis."""
+    x = _f64(x)
+    d = x.shape[-1]
+    s = np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+    assert s.shape == (d,) and d & (d - 1) == 0
+    out = np.empty_like(x)
+    _load().oracle_rotate_rows(_ptr(x), x.size // d, d, _ptr(s), _ptr(out))
+    return out
+
+
+def quantize_blocks(x, block_rows: int):
+    """Per-block e4m3 quantisation of x [B, H, N, d] -> (codes uint8, scales [B, H, nblk])."""
+    x = _f64(x)
+    B, H, N, d = x.shape
+    nblk = (N + block_rows - 1) // block_rows
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty((B, H, nblk), np.float64)
+    _load().oracle_quantize_blocks(_ptr(x), B * H, N, d, int(block_rows), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequantize_blocks(codes, scales, block_rows: int) -> np.ndarray:
+    """Inverse of quantize_blocks in fp64 (code value times its block's scale)."""
+    vals = e4m3_decode(codes)
+    B, H, N, d = vals.shape
+    rep = np.repeat(np.asarray(scales, np.float64), block_rows, axis=2)[:, :, :N]
+    return vals * rep[..., None]
+
+
+def quantize_per_tensor(x):
+    """One scale for the whole tensor: amax/448 (1 if all zero) -> (codes, scale)."""
+    x = _f64(x)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    sc = amax / 448.0 if amax > 0 else 1.0
+    return e4m3_encode(x / sc), sc
+
+
+def fp8_per_tensor_baseline(q, k, v, causal: bool = False, scale: float | None = None, rows=None):
+    """Comparison baseline R1: per-tensor e4m3 Q, K, V (no rotation), P through
+    e4m3(p*256)/256, everything else fp64 ("standard attention FP8, per-tensor
+    scale" of the FP8 error comparison)."""
+    deq = []
+    for x in (q, k, v):
+        c, sc = quantize_per_tensor(x)
+        deq.append(e4m3_decode(c) * sc)
+    return attn_fwd(deq[0], deq[1], deq[2], causal=causal, scale=scale, rows=rows, p_quant=True)

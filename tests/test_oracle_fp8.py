@@ -1,0 +1,115 @@
+"""Pins of the oracle's FP8 pieces: the OCP e4m3fn codec, the Hadamard rotation
+and block quantisation ("FlashAttention-3: Fast and Accurate Attention with
+Asynchrony and Low-precision", sec. 技術 3: FP8 e4m3, per-block scales,
+M = diag(+-1) * Hadamard with (QM)(KM)^T = QK^T).
+
+Checked against library routines (torch.float8_e4m3fn casts, scipy's Sylvester
+Hadamard matrix) and against closed forms (orthogonality, exact round trip of
+every code, ties-to-even at every midpoint, saturation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth_inputs import hadamard_signs
+
+
+def _torch_decode_all():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_decode_matches_torch_all_codes():
+    ours = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    ref = _torch_decode_all()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.nanmax(ours) == 448.0 and np.nanmin(ours) == -448.0
+    assert ours[1] == 2.0 ** -9          # smallest subnormal
+
+
+def test_round_trip_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    back = oracle.e4m3_encode(oracle.e4m3_decode(codes))
+    assert np.array_equal(back, codes)
+
+
+def test_midpoints_round_to_even():
+    vals = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))   # 0 .. 448, increasing
+    mids = (vals[:-1] + vals[1:]) / 2
+    got = oracle.e4m3_encode(mids)
+    lo = np.arange(0, 0x7E)
+    want = np.where(lo % 2 == 0, lo, lo + 1)
+    assert np.array_equal(got, want.astype(np.uint8))
+    ref = torch.from_numpy(mids).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_encode_matches_torch_random():
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.standard_normal(20000) * s for s in (1e-3, 0.05, 1, 30, 150)])
+    x = np.clip(x, -460, 460)
+    ours = oracle.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_saturation_and_nan():
+    got = oracle.e4m3_encode(np.array([449.0, 1e9, np.inf, -500.0, -np.inf, np.nan, 464.0]))
+    assert got.tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x7E]
+
+
+@pytest.mark.parametrize("d", [2, 16, 64, 128])
+def test_rotation_matches_scipy_hadamard(d):
+    from scipy.linalg import hadamard
+    signs = hadamard_signs(d)
+    eye = np.eye(d)
+    rot = oracle.rotate(eye, signs)         # rows: e_i -> s_i H[i, :] / sqrt(d)
+    want = np.diag(signs.astype(np.float64)) @ hadamard(d).astype(np.float64) / np.sqrt(d)
+    assert np.max(np.abs(rot - want)) <= 1e-15
+    assert np.max(np.abs(rot @ rot.T - eye)) <= 1e-14      # orthogonal
+
+
+def test_rotation_preserves_scores():
+    g = np.random.default_rng(1)
+    q = g.standard_normal((3, 128))
+    k = g.standard_normal((5, 128))
+    s = hadamard_signs(128)
+    qm, km = oracle.rotate(q, s), oracle.rotate(k, s)
+    assert np.max(np.abs(qm @ km.T - q @ k.T)) <= 1e-12
+
+
+def test_quantize_blocks_properties():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((1, 2, 70, 16))
+    x[0, 1, 64:] = 0.0                       # an all-zero short block
+    codes, scales = oracle.quantize_blocks(x, 32)
+    assert scales.shape == (1, 2, 3)
+    assert scales[0, 1, 2] == 1.0 and np.all(codes[0, 1, 64:] == 0)
+    vals = oracle.e4m3_decode(codes)
+    for h in range(2):
+        for b in range(3):
+            blk = x[0, h, 32 * b: 32 * b + 32]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                continue
+            assert scales[0, h, b] == amax / 448.0
+            vb = vals[0, h, 32 * b: 32 * b + 32]
+            assert np.max(np.abs(vb)) == 448.0           # the amax element maps to 448
+    deq = oracle.dequantize_blocks(codes, scales, 32)
+    # relative error of e4m3 RNE for normals is at most 2^-4
+    nz = np.abs(x) > 0
+    rel = np.abs(deq - x)[nz] / np.maximum(np.abs(x)[nz], 2 ** -6 * np.repeat(scales, 32, axis=2)[:, :, :70, None].repeat(16, -1)[nz])
+    assert np.max(rel) <= 2 ** -4 + 1e-12
+
+
+def test_per_tensor_baseline_is_worse_than_exact_on_outliers():
+    from synth_inputs import normal_qkv
+    q, k, v = normal_qkv(1, 1, 256, 64, 9, outliers=True)
+    o, _ = oracle.attn_fwd(q, k, v)
+    o1, _ = oracle.fp8_per_tensor_baseline(q, k, v)
+    rmse = np.sqrt(np.mean((o1 - o) ** 2))
+    assert 1e-4 < rmse < 0.2
