@@ -1,0 +1,219 @@
+"""Python binding of libflashattn.so, the gfx950 fused exact-attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/flash_attn.h``.  PyTorch is used
+for device memory and the current stream.  The functions carry the C names:
+
+    flash_attn_fwd(q, k, v, causal=False, scale=None) -> (o, lse)
+    flash_attn_fp8_quantize(x, rotate, signs, block_rows) -> (x_fp8, scales)
+    flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal, scale) -> (o_bf16, lse)
+
+If the shared library is missing this module raises on first use: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = [
+    "FlashAttnError", "lib_path", "load", "flash_attn_fwd", "flash_attn_fp8_quantize",
+    "flash_attn_fwd_fp8", "flash_attn_fp8_block_rows", "flash_attn_status_str",
+    "flash_attn_last_error", "flash_attn_abi_version", "Layout", "FwdOpts", "STATUS",
+    "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libflashattn.so")
+_lock = threading.Lock()
+_lib = None
+
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+STATUS = {
+    0: "FLASH_ATTN_OK", 1: "FLASH_ATTN_ERR_NULL", 2: "FLASH_ATTN_ERR_SHAPE",
+    3: "FLASH_ATTN_ERR_LAYOUT", 4: "FLASH_ATTN_ERR_DTYPE", 5: "FLASH_ATTN_ERR_UNSUPPORTED",
+    6: "FLASH_ATTN_ERR_ARG", 7: "FLASH_ATTN_ERR_WORKSPACE", 8: "FLASH_ATTN_ERR_HIP",
+}
+# Every function include/flash_attn.h declares.
+EXPORTED_SYMBOLS = (
+    "flash_attn_fwd", "flash_attn_fp8_quantize", "flash_attn_fp8_block_rows",
+    "flash_attn_fwd_fp8", "flash_attn_status_str", "flash_attn_last_error",
+    "flash_attn_abi_version",
+)
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(self.name + (f": {detail}" if detail else ""))
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64)]
+
+
+class FwdOpts(ctypes.Structure):
+    _fields_ = [("tau_log2", ctypes.c_float), ("tile_cfg", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libflashattn.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise FlashAttnError(-1, f"{_LIB_PATH} is missing: build it with "
+                                     "exact_attention_77_amd/build.py (or __graft_entry__.build())")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.flash_attn_fwd.argtypes = [P, P, P, P, P, Layout, I, I, F, P, P]
+        lib.flash_attn_fwd.restype = I
+        lib.flash_attn_fp8_quantize.argtypes = [P, I, Layout, I, P, I, P, P, P]
+        lib.flash_attn_fp8_quantize.restype = I
+        lib.flash_attn_fp8_block_rows.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
+        lib.flash_attn_fp8_block_rows.restype = None
+        lib.flash_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, Layout, I, F, P, P]
+        lib.flash_attn_fwd_fp8.restype = I
+        lib.flash_attn_status_str.argtypes = [I]
+        lib.flash_attn_status_str.restype = ctypes.c_char_p
+        lib.flash_attn_last_error.argtypes = []
+        lib.flash_attn_last_error.restype = ctypes.c_char_p
+        lib.flash_attn_abi_version.argtypes = []
+        lib.flash_attn_abi_version.restype = I
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != 0:
+        detail = load().flash_attn_last_error().decode() if status == 8 else ""
+        raise FlashAttnError(status, detail)
+
+
+def flash_attn_status_str(status: int) -> str:
+    return load().flash_attn_status_str(status).decode()
+
+
+def flash_attn_last_error() -> str:
+    return load().flash_attn_last_error().decode()
+
+
+def flash_attn_abi_version() -> int:
+    return int(load().flash_attn_abi_version())
+
+
+def flash_attn_fp8_block_rows():
+    """(rows per Q scale block, rows per K/V scale block) of the fp8 kernel."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    load().flash_attn_fp8_block_rows(ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def _layout_of(t) -> Layout:
+    B, H, N, d = t.shape
+    if d and t.stride(3) != 1:
+        raise FlashAttnError(3, "head_dim must be the contiguous dimension")
+    return Layout(B, H, N, d, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _opts(tau_log2, tile_cfg):
+    if tau_log2 is None and not tile_cfg:
+        return None
+    return ctypes.byref(FwdOpts(-1.0 if tau_log2 is None else float(tau_log2), int(tile_cfg), 0))
+
+
+def flash_attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
+                   tau_log2: float | None = None, tile_cfg: int = 0, out=None, lse=None):
+    """O = softmax(scale * Q K^T) V and the natural-log LSE, on the GPU.
+
+    q, k, v: CUDA tensors [B, H, N, d] (any strides with a contiguous head_dim,
+    so a [B, N, H, d] buffer viewed with .transpose(1, 2) works), all float32 or
+    all bfloat16, same shape and strides.  Returns (o, lse) with o like q and
+    lse float32 [B, H, N].
+    """
+    import torch
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise FlashAttnError(4, f"unsupported dtype {q.dtype}")
+    if not (q.dtype == k.dtype == v.dtype) or not (q.shape == k.shape == v.shape):
+        raise FlashAttnError(2, "q, k, v must share dtype and shape")
+    if q.dim() != 4:
+        raise FlashAttnError(2, "expected [B, H, N, d] tensors")
+    lay = _layout_of(q)
+    if k.stride() != q.stride() or v.stride() != q.stride():
+        raise FlashAttnError(3, "q, k, v must share strides")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    elif out.stride() != q.stride() or out.shape != q.shape or out.dtype != q.dtype:
+        raise FlashAttnError(3, "out must match q's shape, dtype and strides")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d else 1.0
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F32
+    _check(load().flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), lay, dt, int(bool(causal)), float(scale),
+                                 _opts(tau_log2, tile_cfg), _stream()))
+    return out, lse
+
+
+def flash_attn_fp8_quantize(x, rotate: bool, signs=None, block_rows: int | None = None):
+    """Rotate (optionally) and block-quantise x [B, H, N, d] (f32/bf16) to e4m3.
+
+    Returns (x_fp8 uint8 contiguous [B, H, N, d], scales float32 [B, H, nblk]).
+    """
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise FlashAttnError(4, f"unsupported dtype {x.dtype}")
+    B, H, N, d = x.shape
+    if block_rows is None:
+        block_rows = flash_attn_fp8_block_rows()[0]
+    nblk = (N + block_rows - 1) // block_rows
+    out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    sp = signs.data_ptr() if (rotate and signs is not None) else None
+    dt = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
+    _check(load().flash_attn_fp8_quantize(x.data_ptr(), dt, _layout_of(x), int(bool(rotate)), sp,
+                                          int(block_rows), out.data_ptr(), scales.data_ptr(),
+                                          _stream()))
+    return out, scales
+
+
+def flash_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+                       scale: float | None = None, tau_log2: float | None = None,
+                       tile_cfg: int = 0, out=None, lse=None):
+    """FP8 attention on e4m3 inputs with block scales -> (o bf16 [B, H, N, d], lse)."""
+    import torch
+    B, H, N, d = q8.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d else 1.0
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.shape != q8.shape:
+            raise FlashAttnError(3, "fp8 inputs must be contiguous uint8 [B, H, N, d]")
+    _check(load().flash_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(),
+                                     q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                                     out.data_ptr(), lse.data_ptr(), _layout_of(out),
+                                     int(bool(causal)), float(scale), _opts(tau_log2, tile_cfg),
+                                     _stream()))
+    return out, lse

@@ -1,0 +1,203 @@
+// api.cpp -- the C ABI of include/flash_attn.h: host-side validation and
+// dispatch to the gfx950 kernels.  Every check runs before the first HIP call,
+// so argument errors are reported without touching the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/flash_attn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+flash_attn_status hip_status(int err) {
+    if (err == 0) return FLASH_ATTN_OK;
+    snprintf(g_last_error, sizeof(g_last_error), "%s (%d)",
+             hipGetErrorString(static_cast<hipError_t>(err)), err);
+    return FLASH_ATTN_ERR_HIP;
+}
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_empty(const flash_attn_layout& L) {
+    return L.batch == 0 || L.heads == 0 || L.seqlen == 0;
+}
+
+// Shape checks shared by all entry points.  Returns OK for a valid (possibly
+// empty) shape.
+flash_attn_status check_shape(const flash_attn_layout& L) {
+    if (L.batch < 0 || L.heads < 0 || L.seqlen < 0 || L.head_dim < 0) return FLASH_ATTN_ERR_SHAPE;
+    if (L.seqlen > kMaxRows) return FLASH_ATTN_ERR_SHAPE;
+    if (L.batch > kMaxRows || L.heads > kMaxRows || L.batch * L.heads > kMaxRows)
+        return FLASH_ATTN_ERR_SHAPE;
+    if (is_empty(L)) return FLASH_ATTN_OK;
+    if (L.head_dim != 64 && L.head_dim != 128) return FLASH_ATTN_ERR_UNSUPPORTED;
+    return FLASH_ATTN_OK;
+}
+
+// Strides must keep every row 16-byte aligned and must not make rows of
+// different (b, h, i) overlap in a way that aliases the output.
+flash_attn_status check_strides(const flash_attn_layout& L, int64_t elt_bytes) {
+    const int64_t vec = 16 / elt_bytes;
+    if (L.stride_s < L.head_dim || L.stride_h < 0 || L.stride_b < 0) return FLASH_ATTN_ERR_LAYOUT;
+    if (L.stride_s % vec || L.stride_h % vec || L.stride_b % vec) return FLASH_ATTN_ERR_LAYOUT;
+    // Distinct (b, h) must address distinct rows when there is more than one.
+    if (L.heads > 1 && L.stride_h < L.head_dim) return FLASH_ATTN_ERR_LAYOUT;
+    if (L.batch > 1 && L.stride_b < L.head_dim) return FLASH_ATTN_ERR_LAYOUT;
+    return FLASH_ATTN_OK;
+}
+
+flash_attn_status check_opts(const flash_attn_fwd_opts* opts, float* tau, int* tile_cfg) {
+    *tau = 8.0f;
+    *tile_cfg = 0;
+    if (!opts) return FLASH_ATTN_OK;
+    if (opts->reserved != 0) return FLASH_ATTN_ERR_ARG;
+    if (isnan(opts->tau_log2)) return FLASH_ATTN_ERR_ARG;
+    if (opts->tau_log2 >= 0.0f) {
+        if (!(opts->tau_log2 <= 64.0f)) return FLASH_ATTN_ERR_ARG;
+        *tau = opts->tau_log2;
+    }
+    if (opts->tile_cfg < 0 || opts->tile_cfg > 3) return FLASH_ATTN_ERR_ARG;
+    *tile_cfg = opts->tile_cfg;
+    return FLASH_ATTN_OK;
+}
+
+flash_attn_status check_scale(float scale) {
+    if (!isfinite(scale) || !(scale > 0.0f)) return FLASH_ATTN_ERR_ARG;
+    // scale * log2(e) must stay finite.
+    if (!isfinite(scale * 1.4426950408889634f)) return FLASH_ATTN_ERR_ARG;
+    return FLASH_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flash_attn_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, flash_attn_layout layout,
+                                 flash_attn_dtype dtype, int causal, float scale,
+                                 const flash_attn_fwd_opts* opts, void* stream) {
+    flash_attn_status st = check_shape(layout);
+    if (st != FLASH_ATTN_OK) return st;
+    if (dtype != FLASH_ATTN_F32 && dtype != FLASH_ATTN_BF16) return FLASH_ATTN_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return FLASH_ATTN_ERR_ARG;
+    if ((st = check_scale(scale)) != FLASH_ATTN_OK) return st;
+    float tau;
+    int tile_cfg;
+    if ((st = check_opts(opts, &tau, &tile_cfg)) != FLASH_ATTN_OK) return st;
+    if (is_empty(layout)) return FLASH_ATTN_OK;
+    if (!q || !k || !v || !o || !lse) return FLASH_ATTN_ERR_NULL;
+    const int64_t eb = (dtype == FLASH_ATTN_F32) ? 4 : 2;
+    if ((st = check_strides(layout, eb)) != FLASH_ATTN_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return FLASH_ATTN_ERR_LAYOUT;
+
+    fa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.sb = layout.stride_b; a.sh = layout.stride_h; a.ss = layout.stride_s;
+    a.B = static_cast<int32_t>(layout.batch);
+    a.H = static_cast<int32_t>(layout.heads);
+    a.N = static_cast<int32_t>(layout.seqlen);
+    a.D = static_cast<int32_t>(layout.head_dim);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.tau = tau;
+    a.causal = causal;
+    a.tile_cfg = tile_cfg;
+    const int err = (dtype == FLASH_ATTN_BF16) ? fa::launch_fwd_bf16(a, stream)
+                                               : fa::launch_fwd_f32(a, stream);
+    return hip_status(err);
+}
+
+flash_attn_status flash_attn_fp8_quantize(const void* x, flash_attn_dtype in_dtype,
+                                          flash_attn_layout layout, int rotate,
+                                          const int8_t* signs, int block_rows,
+                                          uint8_t* x_fp8, float* scales, void* stream) {
+    flash_attn_status st = check_shape(layout);
+    if (st != FLASH_ATTN_OK) return st;
+    if (in_dtype != FLASH_ATTN_F32 && in_dtype != FLASH_ATTN_BF16) return FLASH_ATTN_ERR_DTYPE;
+    if (rotate != 0 && rotate != 1) return FLASH_ATTN_ERR_ARG;
+    if (block_rows != fa::kFp8QBlock && block_rows != fa::kFp8KVBlock) return FLASH_ATTN_ERR_ARG;
+    if (is_empty(layout)) return FLASH_ATTN_OK;
+    if (!x || !x_fp8 || !scales || (rotate && !signs)) return FLASH_ATTN_ERR_NULL;
+    const int64_t eb = (in_dtype == FLASH_ATTN_F32) ? 4 : 2;
+    if ((st = check_strides(layout, eb)) != FLASH_ATTN_OK) return st;
+    if (!aligned16(x) || !aligned16(x_fp8) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+        return FLASH_ATTN_ERR_LAYOUT;
+    fa::QuantArgs a;
+    a.x = x; a.in_bf16 = (in_dtype == FLASH_ATTN_BF16);
+    a.sb = layout.stride_b; a.sh = layout.stride_h; a.ss = layout.stride_s;
+    a.B = static_cast<int32_t>(layout.batch);
+    a.H = static_cast<int32_t>(layout.heads);
+    a.N = static_cast<int32_t>(layout.seqlen);
+    a.D = static_cast<int32_t>(layout.head_dim);
+    a.rotate = rotate; a.signs = signs; a.block_rows = block_rows;
+    a.out = x_fp8; a.scales = scales;
+    return hip_status(fa::launch_fp8_quantize(a, stream));
+}
+
+void flash_attn_fp8_block_rows(int* q_block_rows, int* kv_block_rows) {
+    if (q_block_rows) *q_block_rows = fa::kFp8QBlock;
+    if (kv_block_rows) *kv_block_rows = fa::kFp8KVBlock;
+}
+
+flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* v_scale, void* o, float* lse,
+                                     flash_attn_layout o_layout, int causal, float scale,
+                                     const flash_attn_fwd_opts* opts, void* stream) {
+    flash_attn_status st = check_shape(o_layout);
+    if (st != FLASH_ATTN_OK) return st;
+    if (causal != 0 && causal != 1) return FLASH_ATTN_ERR_ARG;
+    if ((st = check_scale(scale)) != FLASH_ATTN_OK) return st;
+    float tau;
+    int tile_cfg;
+    if ((st = check_opts(opts, &tau, &tile_cfg)) != FLASH_ATTN_OK) return st;
+    if (is_empty(o_layout)) return FLASH_ATTN_OK;
+    if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse)
+        return FLASH_ATTN_ERR_NULL;
+    if ((st = check_strides(o_layout, 2)) != FLASH_ATTN_OK) return st;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(q_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+        return FLASH_ATTN_ERR_LAYOUT;
+    fa::Fp8Args a;
+    a.q = q8; a.k = k8; a.v = v8; a.qs = q_scale; a.ks = k_scale; a.vs = v_scale;
+    a.o = o; a.lse = lse;
+    a.osb = o_layout.stride_b; a.osh = o_layout.stride_h; a.oss = o_layout.stride_s;
+    a.B = static_cast<int32_t>(o_layout.batch);
+    a.H = static_cast<int32_t>(o_layout.heads);
+    a.N = static_cast<int32_t>(o_layout.seqlen);
+    a.D = static_cast<int32_t>(o_layout.head_dim);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.tau = tau;
+    a.causal = causal;
+    a.tile_cfg = tile_cfg;
+    return hip_status(fa::launch_fwd_fp8(a, stream));
+}
+
+const char* flash_attn_status_str(flash_attn_status s) {
+    switch (s) {
+        case FLASH_ATTN_OK: return "FLASH_ATTN_OK";
+        case FLASH_ATTN_ERR_NULL: return "FLASH_ATTN_ERR_NULL";
+        case FLASH_ATTN_ERR_SHAPE: return "FLASH_ATTN_ERR_SHAPE";
+        case FLASH_ATTN_ERR_LAYOUT: return "FLASH_ATTN_ERR_LAYOUT";
+        case FLASH_ATTN_ERR_DTYPE: return "FLASH_ATTN_ERR_DTYPE";
+        case FLASH_ATTN_ERR_UNSUPPORTED: return "FLASH_ATTN_ERR_UNSUPPORTED";
+        case FLASH_ATTN_ERR_ARG: return "FLASH_ATTN_ERR_ARG";
+        case FLASH_ATTN_ERR_WORKSPACE: return "FLASH_ATTN_ERR_WORKSPACE";
+        case FLASH_ATTN_ERR_HIP: return "FLASH_ATTN_ERR_HIP";
+    }
+    return "FLASH_ATTN_ERR_UNKNOWN";
+}
+
+const char* flash_attn_last_error(void) { return g_last_error; }
+
+int flash_attn_abi_version(void) { return FLASH_ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// internal.h -- shared between the host API and the kernel translation units.
+// Not part of the public ABI (include/flash_attn.h is).
+#pragma once
+#include <stdint.h>
+
+namespace fa {
+
+// Arguments of one forward launch, already validated by the host API.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;          // contiguous [B, H, N]
+    int64_t sb, sh, ss;  // element strides shared by q, k, v, o (head_dim stride 1)
+    int32_t B, H, N, D;
+    float scale_log2;    // softmax scale times log2(e): scores go straight to exp2
+    float tau;           // conditional-rescale threshold, log2 units
+    int32_t causal;
+    int32_t tile_cfg;
+};
+
+// FP8 pre-pass arguments.
+struct QuantArgs {
+    const void* x;
+    int32_t in_bf16;      // 1: x is bf16, 0: x is f32
+    int64_t sb, sh, ss;   // strides of x (elements)
+    int32_t B, H, N, D;
+    int32_t rotate;
+    const int8_t* signs;  // [D] +-1 (device)
+    int32_t block_rows;
+    uint8_t* out;         // contiguous [B, H, N, D]
+    float* scales;        // [B, H, ceil(N / block_rows)]
+};
+
+// FP8 attention arguments.
+struct Fp8Args {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;      // contiguous [B, H, N, D]
+    const float* qs;
+    const float* ks;
+    const float* vs;       // per-block scales
+    void* o;               // bf16, strides below
+    float* lse;
+    int64_t osb, osh, oss;
+    int32_t B, H, N, D;
+    float scale_log2;
+    float tau;
+    int32_t causal;
+    int32_t tile_cfg;
+};
+
+// Launchers: return a hipError_t value (0 = success).
+int launch_fwd_bf16(const FwdArgs& a, void* stream);
+int launch_fwd_f32(const FwdArgs& a, void* stream);
+int launch_fp8_quantize(const QuantArgs& a, void* stream);
+int launch_fwd_fp8(const Fp8Args& a, void* stream);
+
+// Rows per scale block the fp8 attention kernel is built for.
+constexpr int kFp8QBlock = 128;
+constexpr int kFp8KVBlock = 64;
+
+}  // namespace fa

@@ -1,0 +1,157 @@
+/*
+ * flash_attn.h -- C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * What is computed.  For every batch b, head h and query row i:
+ *     s_ij  = scale * <q_i, k_j>                  (j allowed)
+ *     P_ij  = exp(s_ij - m_i) / l_i,   m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i)
+ *     o_i   = sum_j P_ij v_j,          LSE_i = m_i + ln(l_i)   (natural log)
+ * i.e. O = softmax(scale * Q K^T) V plus the per-row log-sum-exp, as defined in
+ * "FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析" sec. 2.1
+ * (standard attention), sec. 6.1-6.3 (safe / online softmax, the rescaling
+ * identity) and sec. 7.2 (the forward keeps only O and the row statistics for
+ * the backward).  "causal" applies the lower-triangular mask of that page's
+ * sec. 11.3: key j is allowed for query i iff j <= i.  The N x N score matrix
+ * never reaches device memory: the kernels tile K/V and keep the running
+ * maximum and sum on chip (sec. 5, 6.2; FlashAttention-2 loop order, sec. 8.2).
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers to tensors are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory, keeps no mutable global state and never
+ *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and the caller synchronises.
+ *  - Arguments are validated on the host before any HIP call; on any error
+ *    return nothing is enqueued and the outputs are untouched.  A failed kernel
+ *    launch returns FLASH_ATTN_ERR_HIP; flash_attn_last_error() then describes it.
+ *  - Q, K, V and O share one flash_attn_layout: element (b, h, i, c) lives at
+ *    base + b*stride_b + h*stride_h + i*stride_s + c (strides in elements, the
+ *    head_dim stride is 1).  This expresses both [B, H, N, d] and [B, N, H, d].
+ *    Base pointers must be 16-byte aligned and the strides multiples of
+ *    16 bytes' worth of elements (8 for bf16, 4 for f32, 16 for fp8).
+ *  - LSE is always a contiguous fp32 [B, H, N] array.
+ *  - Supported v1: head_dim 64 or 128; seqlen_q == seqlen_k == seqlen.
+ *    A zero batch, heads or seqlen is a valid empty call (returns OK, no work;
+ *    pointers may then be NULL).
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLASH_ATTN_ABI_VERSION 1
+
+typedef enum flash_attn_status {
+    FLASH_ATTN_OK = 0,
+    FLASH_ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    FLASH_ATTN_ERR_SHAPE = 2,       /* a size is negative or beyond the limits below  */
+    FLASH_ATTN_ERR_LAYOUT = 3,      /* strides / alignment not supported              */
+    FLASH_ATTN_ERR_DTYPE = 4,       /* dtype not accepted by this entry point         */
+    FLASH_ATTN_ERR_UNSUPPORTED = 5, /* valid request this build does not implement    */
+    FLASH_ATTN_ERR_ARG = 6,         /* scale / option value out of range              */
+    FLASH_ATTN_ERR_WORKSPACE = 7,   /* workspace missing or too small                 */
+    FLASH_ATTN_ERR_HIP = 8          /* the HIP runtime reported an error              */
+} flash_attn_status;
+
+typedef enum flash_attn_dtype {
+    FLASH_ATTN_F32 = 0,             /* IEEE binary32                                  */
+    FLASH_ATTN_BF16 = 1,            /* bfloat16                                       */
+    FLASH_ATTN_FP8_E4M3 = 2         /* OCP FP8 E4M3FN (bias 7, max 448, no inf)        */
+} flash_attn_dtype;
+
+/* Shape and strides (in elements) shared by Q, K, V and O.
+ * Limits: 0 <= batch*heads <= 2^24, 0 <= seqlen <= 2^24. */
+typedef struct flash_attn_layout {
+    int64_t batch, heads, seqlen, head_dim;
+    int64_t stride_b, stride_h, stride_s;
+} flash_attn_layout;
+
+/* Optional tuning knobs (pass NULL for the defaults).
+ * tau_log2: conditional-rescale threshold in log2 units ("FlashAttention-4"
+ *   explainer, sec. 論文 Section 3.3: the running output is rescaled only when
+ *   the running maximum grows by more than tau).  The result does not depend
+ *   on tau (the rescaling identity, FlashAttention page sec. 6.3) beyond fp32
+ *   rounding; unnormalised probabilities stay below 2^tau.  Range [0, 64];
+ *   a negative value selects the default 8.
+ * tile_cfg: 0 = automatic; other values select an alternative kernel
+ *   configuration (used by tests to cross-check configurations). */
+typedef struct flash_attn_fwd_opts {
+    float tau_log2;
+    int32_t tile_cfg;
+    int32_t reserved;   /* must be 0 */
+} flash_attn_fwd_opts;
+
+/*
+ * Forward attention, fp32 or bf16 in and out.
+ *   q, k, v : [layout] tensors of `dtype` (read only)
+ *   o       : [layout] output of `dtype` (bf16 outputs are rounded to nearest even)
+ *   lse     : fp32 [batch, heads, seqlen] natural-log log-sum-exp of the scaled scores
+ *   causal  : 0 or 1 (lower-triangular mask, key j <= query i)
+ *   scale   : multiplies Q K^T; finite and > 0 (the usual value is 1/sqrt(head_dim))
+ * Errors: NULL -> ERR_NULL; sizes -> ERR_SHAPE; head_dim not 64/128 ->
+ * ERR_UNSUPPORTED; strides/alignment -> ERR_LAYOUT; dtype other than F32/BF16
+ * -> ERR_DTYPE; scale or opts out of range -> ERR_ARG.
+ */
+flash_attn_status flash_attn_fwd(const void* q, const void* k, const void* v,
+                                 void* o, float* lse,
+                                 flash_attn_layout layout, flash_attn_dtype dtype,
+                                 int causal, float scale,
+                                 const flash_attn_fwd_opts* opts, void* stream);
+
+/*
+ * FP8 pre-pass ("FlashAttention-3: Fast and Accurate Attention with Asynchrony
+ * and Low-precision", sec. 技術 3, accuracy part): optional incoherent
+ * processing x -> (x * signs) H_d / sqrt(d) (Sylvester Hadamard H_d, applied as
+ * a fast Walsh-Hadamard transform), then block quantisation: rows of one
+ * (batch, head) are grouped in blocks of `block_rows` consecutive rows, each
+ * block gets scale = amax(block) / 448 (1 for an all-zero block) and every
+ * element becomes e4m3(x / scale) (round to nearest even, saturating at 448).
+ *   x       : [layout] F32 or BF16 input (`in_dtype`)
+ *   rotate  : 1 = apply the rotation (Q and K), 0 = none (V)
+ *   signs   : device int8[head_dim] of +1/-1 (ignored when rotate == 0)
+ *   block_rows : rows per scale block; must equal the value the fp8 attention
+ *              kernel expects (flash_attn_fp8_block_rows)
+ *   x_fp8   : output, contiguous [batch, heads, seqlen, head_dim] e4m3 bytes
+ *   scales  : output, fp32 [batch, heads, ceil(seqlen / block_rows)]
+ */
+flash_attn_status flash_attn_fp8_quantize(const void* x, flash_attn_dtype in_dtype,
+                                          flash_attn_layout layout, int rotate,
+                                          const int8_t* signs, int block_rows,
+                                          uint8_t* x_fp8, float* scales, void* stream);
+
+/* Block sizes (rows per scale) that flash_attn_fwd_fp8 expects for Q and for K/V. */
+void flash_attn_fp8_block_rows(int* q_block_rows, int* kv_block_rows);
+
+/*
+ * FP8 forward attention: e4m3 Q, K, V (as written by flash_attn_fp8_quantize,
+ * contiguous [batch, heads, seqlen, head_dim]) with their per-block fp32
+ * scales; fp32 accumulation; O is bf16 with the strides of `o_layout`
+ * (its batch/heads/seqlen/head_dim give the shape of everything).  Q and K
+ * must have been rotated with the same signs (or both not rotated): the
+ * rotation is orthogonal, so Q K^T is unchanged and V needs no inverse.
+ * Probabilities enter the second product as e4m3 (scaled by 2^8).
+ */
+flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* v_scale,
+                                     void* o, float* lse, flash_attn_layout o_layout,
+                                     int causal, float scale,
+                                     const flash_attn_fwd_opts* opts, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* flash_attn_status_str(flash_attn_status s);
+
+/* Detail of the last FLASH_ATTN_ERR_HIP on the calling thread ("" if none). */
+const char* flash_attn_last_error(void);
+
+/* FLASH_ATTN_ABI_VERSION of the built library. */
+int flash_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/flash_attn.h declares, and rejects bad arguments with the documented
+status codes before any HIP call (pointers here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_77_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flash_attn_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings():
+    assert fa.flash_attn_abi_version() == 1
+    for code, name in fa.STATUS.items():
+        assert fa.flash_attn_status_str(code) == name
+    assert fa.flash_attn_fp8_block_rows() == (128, 64)
+
+
+def _lay(B=1, H=2, N=128, d=64, sb=None, sh=None, ss=None):
+    ss = d if ss is None else ss
+    sh = N * ss if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return fa.Layout(B, H, N, d, sb, sh, ss)
+
+
+P = 4096  # a 16-byte aligned fake address; never dereferenced on these paths
+
+
+def fwd(q=P, k=P, v=P, o=P, lse=P, lay=None, dtype=fa.DTYPE_BF16, causal=0, scale=0.125,
+        opts=None):
+    return fa.load().flash_attn_fwd(q, k, v, o, lse, lay or _lay(), dtype, causal, scale, opts, None)
+
+
+def test_null_pointers():
+    for kw in ("q", "k", "v", "o", "lse"):
+        assert fwd(**{kw: None}) == 1
+
+
+def test_empty_inputs_are_noops():
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, lay=_lay(N=0)) == 0
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, lay=_lay(B=0)) == 0
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, lay=_lay(H=0)) == 0
+
+
+@pytest.mark.parametrize("lay", [_lay(N=-1), _lay(B=-2), _lay(N=(1 << 24) + 1),
+                                 fa.Layout(1 << 13, 1 << 12, 16, 64, 64, 64, 64)])
+def test_bad_shapes(lay):
+    assert fwd(lay=lay) == 2
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_unsupported_head_dim(d):
+    assert fwd(lay=_lay(d=d)) == 5
+
+
+@pytest.mark.parametrize("lay", [_lay(ss=60), _lay(ss=68), _lay(sh=8), _lay(sb=4, H=1, B=2)])
+def test_bad_strides(lay):
+    assert fwd(lay=lay) == 3
+
+
+def test_misaligned_pointers():
+    assert fwd(q=P + 2) == 3
+    assert fwd(o=P + 8) == 3
+    assert fwd(lse=P + 2) == 3
+
+
+def test_bad_dtype():
+    assert fwd(dtype=fa.DTYPE_FP8_E4M3) == 4
+    assert fwd(dtype=7) == 4
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan"), 3e38])
+def test_bad_scale(scale):
+    assert fwd(scale=scale) == 6
+
+
+def test_bad_causal_flag():
+    assert fwd(causal=2) == 6
+
+
+@pytest.mark.parametrize("opts", [fa.FwdOpts(65.0, 0, 0), fa.FwdOpts(float("nan"), 0, 0),
+                                  fa.FwdOpts(8.0, 9, 0), fa.FwdOpts(8.0, 0, 1)])
+def test_bad_options(opts):
+    assert fwd(opts=ctypes.byref(opts)) == 6
+
+
+def test_f32_strides_need_16_bytes():
+    # 4 floats = 16 bytes: stride 68 ok for f32 alignment, 66 is not
+    assert fwd(lay=_lay(ss=66), dtype=fa.DTYPE_F32) == 3
+
+
+def test_quantize_validation():
+    lib = fa.load()
+    lay = _lay()
+    assert lib.flash_attn_fp8_quantize(P, 1, lay, 1, None, 128, P, P, None) == 1
+    assert lib.flash_attn_fp8_quantize(P, 1, lay, 0, None, 100, P, P, None) == 6
+    assert lib.flash_attn_fp8_quantize(P, 2, lay, 0, None, 128, P, P, None) == 4
+    assert lib.flash_attn_fp8_quantize(None, 1, _lay(N=0), 0, None, 128, None, None, None) == 0
+
+
+def test_fp8_fwd_validation():
+    lib = fa.load()
+    lay = _lay()
+    assert lib.flash_attn_fwd_fp8(P, P, P, P, P, P, P, None, lay, 0, 0.1, None, None) == 1
+    assert lib.flash_attn_fwd_fp8(P, P, P, P, P, P, P, P, lay, 0, -0.1, None, None) == 6
+    assert lib.flash_attn_fwd_fp8(P, P, P, P, P, P, P, P, _lay(d=80), 0, 0.1, None, None) == 5
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(fa.FlashAttnError):
+        fa.load()
