@@ -8,7 +8,10 @@
 // (sec. 8.1).  Queries are split across waves, K/V are shared (sec. 8.3).
 // The maximum the exponentials refer to only advances when a tile's maximum
 // exceeds it by more than tau ("FlashAttention-4" explainer, 論文 Section 3.3);
-// the output stays exact by the rescaling identity (sec. 6.3).
+// the output stays exact by the rescaling identity (sec. 6.3).  The score
+// product of the next tile is issued before the softmax of the current one so
+// that matrix-core and vector work overlap (the two-stage GEMM/softmax
+// pipelining of the FlashAttention-3 note, section 技術 2).
 //
 // gfx950 mapping (designed for CDNA4, not taken from the pages' Hopper or
 // Blackwell kernels):
@@ -17,16 +20,23 @@
 //    B = Q^T held in registers for the whole loop).  In the 32x32 accumulator
 //    layout lane l holds column l % 32, i.e. ONE query, and 16 of the keys, so
 //    the row maximum and row sum are in-lane reductions plus one exchange
-//    between lane l and l ^ 32.
+//    between lane l and l ^ 32 (v_permlane32_swap).
 //  * the K rows are fed to the first product in a permuted order (bits 2 and
 //    3 of the row index swapped) so that the accumulator registers of S^T are,
 //    after exp2 and a bf16 conversion, already the B operand of the second
 //    product O^T += V^T P^T: no LDS round trip for P.
 //  * O^T stays in registers with one query per lane, so the rescale factor is
-//    a per-lane scalar.
-//  * K is stored in LDS row-major and V transposed (d-major), both padded so
-//    that the 16-byte operand reads of 16 consecutive rows hit distinct banks;
-//    two buffers let the global loads of tile j+1 overlap the math of tile j.
+//    a per-lane scalar; the row sum is accumulated from the bf16
+//    probabilities with v_dot2 (two per op), the same values that multiply V.
+//  * K and V tiles are copied global -> LDS by the direct-to-LDS loads of
+//    gfx950 (global_load_lds_dwordx4: no registers, no LDS store
+//    instructions), row-major and unpadded.  Each lane picks the 16-byte chunk
+//    it copies so that the stored tile is XOR-swizzled per row; the operand
+//    reads undo the swizzle and hit distinct LDS banks.  V^T is read with the
+//    transposing LDS read (ds_read_b64_tr_b16), which hands each lane four
+//    consecutive keys of one head-dim column.
+//  * K is prefetched two tiles ahead and V one tile ahead (two LDS buffers
+//    each), one workgroup barrier per tile.
 //  * workgroups are renumbered so that the tiles of one head run on one XCD
 //    (the hardware deals workgroup ids round-robin over the 8 XCDs), which
 //    keeps that head's K/V in the XCD's L2; under the causal mask the heaviest
@@ -42,20 +52,28 @@ namespace fa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
 constexpr int BC = 64;  // keys per K/V tile
 constexpr int WQ = 32;  // query rows per wave
+constexpr bf16x2 kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
 template <int D>
-struct Lds {
-    static constexpr int KS = D + 8;   // K row stride (elements)
-    static constexpr int VS = BC + 8;  // V^T row stride (elements)
-    static constexpr int K_ELEMS = BC * KS;
-    static constexpr int V_ELEMS = D * VS;
-    static constexpr int BUF = K_ELEMS + V_ELEMS;
-    static constexpr int BYTES = 2 * BUF * int(sizeof(u16));
+struct Tile {
+    static constexpr int CPR = D / 8;               // 16-byte chunks per row
+    static constexpr int BYTES = BC * D * 2;        // one K or V tile
+    static constexpr int LDS_BYTES = 4 * BYTES;     // K0 K1 V0 V1
+    // XOR swizzles (in 16-byte chunk units) applied to a row's chunk index.
+    // K: 16 lanes read one logical chunk of 16 different rows.
+    __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+    // V: 16 lanes read 4 rows x 32 bytes (two groups: 4 rows x 64 bytes).
+    __device__ static int vswz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
 // Row of the A operand that lane row i loads: bits 2 and 3 swapped.  With this
@@ -67,20 +85,35 @@ __device__ __forceinline__ int perm_row(int i) {
     return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// v_permlane32_swap(x, x) yields {x[lo half] in both halves, x[hi half] in
+// both halves}; combining the two gives the pair value in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
+// Transposing LDS read: within each 16-lane group, destination lane 4p+q gets
+// element q of the 8-byte rows read by source lanes p, 4+p, 8+p, 12+p.
+__device__ __forceinline__ short4_t lds_read_tr(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((__attribute__((address_space(3))) char*)(p)));
+}
+
+// At most 256 registers per lane so that two waves share each SIMD.
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
-    using L = Lds<D>;
-    constexpr int BR = NW * WQ;          // query rows per workgroup
-    constexpr int T = NW * 64;           // threads
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int CH = BC * CPR / T;     // chunks per thread per tile (K and V each)
-    static_assert(CH >= 1 && BC * CPR % T == 0, "tile / thread mismatch");
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_bf16_kernel(FwdArgs a) {
+    using TL = Tile<D>;
+    constexpr int BR = NW * WQ;                       // query rows per workgroup
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
+    constexpr int NI = TL::BYTES / 1024 / NW;         // 1 KB direct loads per wave per tile
+    static_assert(NI >= 1 && TL::BYTES % (1024 * NW) == 0, "tile / wave mismatch");
 
-    extern __shared__ __attribute__((aligned(16))) u16 smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     // ---- work decomposition -------------------------------------------------
     const int n_qt = (a.N + BR - 1) / BR;
@@ -107,9 +140,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int qi = q0 + j;               // this lane's query row
 
     const int n_kt_all = (a.N + BC - 1) / BC;
-    const int kt_end = CAUSAL ? min(n_kt_all, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt_all;
-    int wave_kt_end = CAUSAL ? min(kt_end, (min(a.N, q0 + WQ) + BC - 1) / BC) : kt_end;
-    if (q0 >= a.N) wave_kt_end = 0;
+    const int nt = CAUSAL ? min(n_kt_all, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt_all;
+    int wnt = CAUSAL ? min(nt, (min(a.N, q0 + WQ) + BC - 1) / BC) : nt;
+    if (q0 >= a.N) wnt = 0;
+
+    // ---- direct global -> LDS tile copy ---------------------------------------
+    // Wave w copies 1 KB blocks w*NI .. w*NI+NI-1 of the tile; lane L of a block
+    // fills LDS chunk 64*blk + L, i.e. row (64*blk + L) / CPR, physical chunk
+    // (64*blk + L) % CPR, which holds logical chunk (physical ^ swizzle(row)).
+    // Rows past the end of the sequence re-read the last row: their scores are
+    // masked to -inf, so their probabilities are exactly 0.
+    auto copy_tile = [&](const u16* src, int kt, int lds_off, bool is_k) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int blk = wave * NI + i;
+            const int c = blk * 64 + lane;
+            const int row = c / TL::CPR;
+            const int pch = c % TL::CPR;
+            const int lch = pch ^ (is_k ? TL::kswz(row) : TL::vswz(row));
+            const int key = min(kt * BC + row, a.N - 1);
+            const u16* g = src + int64_t(key) * a.ss + lch * 8;
+            __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + lds_off + blk * 1024), 16, 0, 0);
+        }
+    };
+    auto k_off = [](int buf) { return buf * TL::BYTES; };
+    auto v_off = [](int buf) { return (2 + buf) * TL::BYTES; };
 
     // ---- Q^T operand: lane (query j, half hh) holds Q[qi][16ks + 8hh .. +7] ----
     bf16x8 qreg[KSTEPS];
@@ -129,132 +184,125 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     float lsum = 0.f;        // this lane's share of the running sum
     const float c2 = a.scale_log2;
 
-    // ---- K/V tile staging: global -> registers -> LDS ------------------------
-    uint4 kreg[CH], vreg[CH];
-    auto load_global = [&](int kt) {
+    // per-lane LDS addressing that does not change across tiles
+    const int krow_base = perm_row(j);                              // + 32*st
+    const int tr_row = 8 * (lane >> 5) + ((lane >> 2) & 3);         // + 32*st + 16*cc
+    const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);   // + 4*dt
+    const int tr_half = 8 * (lane & 1);
+
+    // S^T for one K tile (two 32-key subtiles).
+    auto scores = [&](f32x16 (&s)[2], int buf) {
+        const char* kt_lds = smem + k_off(buf);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * T;
-            const int row = c / CPR, col = (c % CPR) * 8;
-            const int key = kt * BC + row;
-            uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
-            if (key < a.N) {
-                kx = *reinterpret_cast<const uint4*>(Kg + int64_t(key) * a.ss + col);
-                vx = *reinterpret_cast<const uint4*>(Vg + int64_t(key) * a.ss + col);
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
+            const int row = 32 * st + krow_base;
+            const char* rp = kt_lds + row * (2 * D);
+            const int sw = TL::kswz(row);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(rp + 16 * ((2 * ks + hh) ^ sw));
+                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[st], 0, 0, 0);
             }
-            kreg[i] = kx;
-            vreg[i] = vx;
-        }
-    };
-    auto store_lds = [&](int buf) {
-        u16* Ks = smem + buf * L::BUF;
-        u16* Vts = Ks + L::K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * T;
-            const int row = c / CPR, col = (c % CPR) * 8;
-            *reinterpret_cast<uint4*>(Ks + row * L::KS + col) = kreg[i];
-            const u16* v8 = reinterpret_cast<const u16*>(&vreg[i]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Vts[(col + e) * L::VS + row] = v8[e];
         }
     };
 
-    if (kt_end > 0) {
-        load_global(0);
-        store_lds(0);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < kt_end; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < kt_end) load_global(kt + 1);
-
-        if (kt < wave_kt_end) {
-            const u16* Ks = smem + buf * L::BUF;
-            const u16* Vts = Ks + L::K_ELEMS;
-
-            // S^T = K Q^T for keys kt*BC + [0, 32) and [32, 64)
-            f32x16 s[2];
+    // Softmax of tile kt's scores and O^T += V^T P^T, with the score product
+    // of the next tile (into nxt, from K buffer nbuf) issued in the same
+    // straight-line block so the scheduler can interleave MFMA and VALU work.
+    // On a wave's last tile the extra product reads a valid but unused buffer.
+    auto softmax_pv = [&](f32x16 (&s)[2], int kt, int buf, f32x16 (&nxt)[2], int nbuf) {
+        const int k_lo = kt * BC;
+        if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
-                const u16* krow = Ks + (32 * st + perm_row(j)) * L::KS + 8 * hh;
+                for (int g = 0; g < 16; ++g) {
+                    const int r = g >> 2, t = g & 3;
+                    const int key = k_lo + 32 * st + 16 * (r >> 1) + 8 * hh + 4 * (r & 1) + t;
+                    if (key >= a.N || (CAUSAL && key > qi)) s[st][g] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-                    s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[st], 0, 0, 0);
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) mx = fmaxf(mx, s[st][g]);
+        mx = pair_max(mx);
+        const float mt = mx * c2;
+        if (__any(mt > m_ref + a.tau)) {  // wave-uniform: rescaling is always exact
+            const float mn = fmaxf(m_ref, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
+            m_ref = mn;
+        }
+        const float neg_m = -m_ref;
+        scores(nxt, nbuf);
+        const char* vt_lds = smem + v_off(buf);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                bf16x8 pb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pb[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[st][8 * cc + e], c2, neg_m)));
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const bf16x2 pr = {pb[e], pb[e + 1]};
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lsum, false);
+                }
+                // A operand (32 head-dim rows x 16 keys) from two transposing
+                // reads: lane 16g + 4a + b addresses key 8*(g >> 1) + a (+4),
+                // columns 16*(g & 1) + 4b .. +3 of the row-major V tile.
+                const int row = 32 * st + 16 * cc + tr_row;
+                const char* rp = vt_lds + row * (2 * D) + tr_half;
+                const int sw = TL::vswz(row);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const char* p = rp + 16 * ((4 * dt + tr_lch) ^ sw);
+                    const short4_t lo = lds_read_tr(p);
+                    const short4_t hi = lds_read_tr(p + 4 * (2 * D));
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
                 }
             }
+    };
 
-            // masking: causal diagonal tiles and the ragged end of the keys
-            const int k_lo = kt * BC;
-            const bool need_mask = (k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0);
-            if (need_mask) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int g = 0; g < 16; ++g) {
-                        const int r = g >> 2, t = g & 3;
-                        const int key = k_lo + 32 * st + 16 * (r >> 1) + 8 * hh + 4 * (r & 1) + t;
-                        const bool masked = key >= a.N || (CAUSAL && key > qi);
-                        if (masked) s[st][g] = -INFINITY;
-                    }
-            }
+    // ---- prologue: K0, V0, K1 in flight; S(0) ---------------------------------
+    if (nt > 0) {
+        copy_tile(Kg, 0, k_off(0), true);
+        copy_tile(Vg, 0, v_off(0), false);
+    }
+    if (nt > 1) copy_tile(Kg, 1, k_off(1), true);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-            // online softmax, base 2, conditional rescale (wave-uniform decision)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int g = 0; g < 16; ++g) mx = fmaxf(mx, s[st][g]);
-            mx = fmaxf(mx, xor32(mx));
-            const float mt = mx * c2;
-            const bool need = mt > m_ref + a.tau;
-            if (__any(need)) {
-                const float mn = fmaxf(m_ref, mt);
-                const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
-                lsum *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
-                m_ref = mn;
-            }
-            bf16x8 pb[2][2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[st][8 * cc + e], c2, -m_ref));
-                        lsum += p;
-                        pb[st][cc][e] = static_cast<__bf16>(p);
-                    }
+    f32x16 sA[2], sB[2];
+    if (wnt > 0) scores(sA, 0);
+    __syncthreads();  // every wave is done with K0 before K2 overwrites it
 
-            // O^T += V^T P^T
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u16* vrow = Vts + (32 * dt + j) * L::VS + 8 * hh;
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + 32 * st + 16 * cc);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st][cc], oacc[dt], 0, 0, 0);
-                    }
-            }
-        }
-
-        if (kt + 1 < kt_end) store_lds(buf ^ 1);
+    // ---- main loop, unrolled by two so the score buffers alternate -----------
+    auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        if (kt + 2 < nt) copy_tile(Kg, kt + 2, k_off(kt & 1), true);
+        if (kt + 1 < nt) copy_tile(Vg, kt + 1, v_off((kt + 1) & 1), false);
+        if (kt < wnt) softmax_pv(cur, kt, kt & 1, nxt, (kt + 1) & 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int kt = 0; kt < nt; kt += 2) {
+        step(kt, sA, sB);
+        if (kt + 1 < nt) step(kt + 1, sB, sA);
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
-    if (qi < a.N && wave_kt_end > 0) {
-        const float lt = lsum + xor32(lsum);
+    if (qi < a.N && wnt > 0) {
+        const float lt = pair_sum(lsum);
         const float inv = 1.0f / lt;
         u16* orow = Og + int64_t(qi) * a.ss;
 #pragma unroll
@@ -272,19 +320,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, int NW, bool CAUSAL>
 int launch(const FwdArgs& a, hipStream_t stream) {
-    using L = Lds<D>;
     constexpr int BR = NW * WQ;
+    constexpr int LDS = Tile<D>::LDS_BYTES;
     auto kern = fwd_bf16_kernel<D, NW, CAUSAL>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
         if (e != hipSuccess) return static_cast<int>(e);
         attr_set = true;
     }
     const int n_qt = (a.N + BR - 1) / BR;
     const int64_t grid = int64_t(n_qt) * a.B * a.H;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), L::BYTES, stream, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), LDS, stream, a);
     return static_cast<int>(hipGetLastError());
 }
 
