@@ -38,6 +38,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-cfg", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run plain device copies of this size (MiB) so that "
+                         "HBM byte counters can be scaled against a known transfer")
     return ap.parse_args()
 
 
@@ -147,6 +150,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": None, "kernel_ms": round(ms_ev, 5)},
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

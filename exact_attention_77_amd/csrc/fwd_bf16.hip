@@ -134,7 +134,8 @@ void fwd_bf16_kernel(FwdArgs a) {
     u16* Og = static_cast<u16*>(a.o) + base;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int j = lane & 31, hh = lane >> 5;
     const int q0 = qt * BR + wave * WQ;  // first query row of this wave
     const int qi = q0 + j;               // this lane's query row
@@ -148,23 +149,39 @@ void fwd_bf16_kernel(FwdArgs a) {
     // Wave w copies 1 KB blocks w*NI .. w*NI+NI-1 of the tile; lane L of a block
     // fills LDS chunk 64*blk + L, i.e. row (64*blk + L) / CPR, physical chunk
     // (64*blk + L) % CPR, which holds logical chunk (physical ^ swizzle(row)).
-    // Rows past the end of the sequence re-read the last row: their scores are
-    // masked to -inf, so their probabilities are exactly 0.
-    auto copy_tile = [&](const u16* src, int kt, int lds_off, bool is_k) {
+    // The row a lane copies is the same in every tile, so its source pointer
+    // is fixed and a tile adds a wave-uniform offset.  In the ragged last tile
+    // rows past the end re-read the last row: their scores are masked to -inf,
+    // so their probabilities are exactly 0.
+    int crow[NI];
+    const u16* kp[NI];
+    const u16* vp[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int blk = wave * NI + i;
-            const int c = blk * 64 + lane;
-            const int row = c / TL::CPR;
-            const int pch = c % TL::CPR;
-            const int lch = pch ^ (is_k ? TL::kswz(row) : TL::vswz(row));
-            const int key = min(kt * BC + row, a.N - 1);
-            const u16* g = src + int64_t(key) * a.ss + lch * 8;
-            __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + lds_off + blk * 1024), 16, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+        const int c = (wave * NI + i) * 64 + lane;
+        crow[i] = c / TL::CPR;
+        const int pch = c % TL::CPR;
+        kp[i] = Kg + int64_t(crow[i]) * a.ss + 8 * (pch ^ TL::kswz(crow[i]));
+        vp[i] = Vg + int64_t(crow[i]) * a.ss + 8 * (pch ^ TL::vswz(crow[i]));
+    }
+    auto copy_tile = [&](const u16* const (&src)[NI], int kt, int lds_off) {
+        const int k0 = kt * BC;
+        if (k0 + BC <= a.N) {  // full tile: one wave-uniform offset
+            const int64_t off = int64_t(k0) * a.ss;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(src[i] + off),
+                                                 (lds_void*)(smem + lds_off + (wave * NI + i) * 1024), 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int64_t row_off = int64_t(min(k0 + crow[i], a.N - 1) - crow[i]);
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(src[i] + row_off * a.ss),
+                                                 (lds_void*)(smem + lds_off + (wave * NI + i) * 1024), 16, 0, 0);
+            }
         }
     };
-    auto k_off = [](int buf) { return buf * TL::BYTES; };
-    auto v_off = [](int buf) { return (2 + buf) * TL::BYTES; };
+    constexpr int K_OFF0 = 0, K_OFF1 = TL::BYTES, V_OFF0 = 2 * TL::BYTES, V_OFF1 = 3 * TL::BYTES;
 
     // ---- Q^T operand: lane (query j, half hh) holds Q[qi][16ks + 8hh .. +7] ----
     bf16x8 qreg[KSTEPS];
@@ -190,48 +207,69 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);   // + 4*dt
     const int tr_half = 8 * (lane & 1);
 
-    // S^T for one K tile (two 32-key subtiles).
-    auto scores = [&](f32x16 (&s)[2], int buf) {
-        const char* kt_lds = smem + k_off(buf);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
-            const int row = 32 * st + krow_base;
-            const char* rp = kt_lds + row * (2 * D);
-            const int sw = TL::kswz(row);
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(rp + 16 * ((2 * ks + hh) ^ sw));
-                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[st], 0, 0, 0);
-            }
-        }
+    // K operand of score MFMA m (subtile m % 2, k-step m / 2: consecutive
+    // MFMAs accumulate into different subtiles).
+    auto k_operand = [&](const char* kt_lds, int m) -> bf16x8 {
+        const int st = m & 1, ks = m >> 1;
+        const int row = 32 * st + krow_base;
+        return *reinterpret_cast<const bf16x8*>(kt_lds + row * (2 * D) + 16 * ((2 * ks + hh) ^ TL::kswz(row)));
+    };
+    // V^T operand of PV MFMA n (key chunk c = n / DT, head-dim tile dt = n % DT):
+    // two transposing reads; lane 16g + 4a + b addresses key 8*(g >> 1) + a
+    // (+4), columns 16*(g & 1) + 4b .. +3 of the row-major V tile.
+    auto v_operand = [&](const char* vt_lds, int n) -> bf16x8 {
+        const int c = n / DT, dt = n % DT;
+        const int row = 32 * (c >> 1) + 16 * (c & 1) + tr_row;
+        const char* p = vt_lds + row * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ TL::vswz(row));
+        const short4_t lo = lds_read_tr(p);
+        const short4_t hi = lds_read_tr(p + 4 * (2 * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // Softmax of tile kt's scores and O^T += V^T P^T, with the score product
-    // of the next tile (into nxt, from K buffer nbuf) issued in the same
-    // straight-line block so the scheduler can interleave MFMA and VALU work.
-    // On a wave's last tile the extra product reads a valid but unused buffer.
-    auto softmax_pv = [&](f32x16 (&s)[2], int kt, int buf, f32x16 (&nxt)[2], int nbuf) {
+    // S^T for one K tile (two 32-key subtiles); used outside the main loop.
+    auto scores = [&](f32x16 (&s)[2], const char* kt_lds) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
+#pragma unroll
+        for (int m = 0; m < 2 * KSTEPS; ++m)
+            s[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kt_lds, m), qreg[m >> 1], s[m & 1], 0, 0, 0);
+    };
+
+    // Causal diagonal / ragged tiles: scores of keys past the query (or past
+    // the end) become -inf.  Register g of subtile st in lane half hh holds key
+    // k_lo + off(st, g) + 8*hh with a compile-time off, so one per-lane
+    // threshold decides every register.
+    auto apply_mask = [&](f32x16 (&s)[2], int kt) {
+        const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - kt * BC - 8 * hh;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                const int r = g >> 2, t = g & 3;
+                const int off = 32 * st + 16 * (r >> 1) + 4 * (r & 1) + t;
+                if (off > lim) s[st][g] = -INFINITY;
+            }
+    };
+    auto needs_mask = [&](int kt) {
         const int k_lo = kt * BC;
-        if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int g = 0; g < 16; ++g) {
-                    const int r = g >> 2, t = g & 3;
-                    const int key = k_lo + 32 * st + 16 * (r >> 1) + 8 * hh + 4 * (r & 1) + t;
-                    if (key >= a.N || (CAUSAL && key > qi)) s[st][g] = -INFINITY;
-                }
-        }
+        return (k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0);
+    };
+    auto tile_max = [&](const f32x16 (&s)[2]) -> float {
         float mx = -INFINITY;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int g = 0; g < 16; ++g) mx = fmaxf(mx, s[st][g]);
-        mx = pair_max(mx);
+        return pair_max(mx);
+    };
+
+    // The reference maximum advances only when the tile maximum exceeds it by
+    // more than tau; the decision is wave-uniform (rescaling is always exact).
+    auto advance_max = [&](float mx) {
         const float mt = mx * c2;
-        if (__any(mt > m_ref + a.tau)) {  // wave-uniform: rescaling is always exact
+        if (__any(mt > m_ref + a.tau)) {
             const float mn = fmaxf(m_ref, mt);
             const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
             lsum *= alpha;
@@ -241,63 +279,109 @@ void fwd_bf16_kernel(FwdArgs a) {
                 for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
             m_ref = mn;
         }
+    };
+
+    // One straight-line block per tile, issued in fenced chunks so that every
+    // matrix-core instruction has independent vector work beside it:
+    //  phase 1: score MFMAs of the next tile (K operands read NPK MFMAs ahead),
+    //           each paired with probabilities of the current tile
+    //           (fma, exp2, bf16 pack, row-sum dot2);
+    //  phase 2: PV MFMAs of the current tile (V^T operands read NPV ahead),
+    //           each paired with part of the next tile's row maximum (a tile
+    //           that needs a mask gets it, and its maximum, afterwards).
+    // On a wave's last tile the score product reads a valid but unused buffer.
+    constexpr int QKM = 2 * KSTEPS;   // score MFMAs per tile
+    constexpr int PVM = 4 * DT;       // PV MFMAs per tile
+    constexpr int NPAIR = 16;         // probability pairs per lane per tile
+    constexpr int PPM = NPAIR / QKM;  // pairs per score MFMA
+    constexpr int NPK = 2, NPV = 2;
+    static_assert(NPAIR % QKM == 0 && 16 % PVM == 0, "phase split");
+    auto main_block = [&](f32x16 (&s)[2], const char* vt_lds, f32x16 (&nxt)[2], const char* knext) -> float {
         const float neg_m = -m_ref;
-        scores(nxt, nbuf);
-        const char* vt_lds = smem + v_off(buf);
+        bf16x8 pb[4];
+        bf16x8 kb[NPK];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int i = 0; i < NPK; ++i) kb[i] = k_operand(knext, i);
+        const f32x16 zero = {};
+        float lpart[2] = {0.f, 0.f};  // two independent row-sum chains
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                bf16x8 pb;
+        for (int m = 0; m < QKM; ++m) {
+            const bf16x8 ka = kb[m % NPK];
+            if (m + NPK < QKM) kb[m % NPK] = k_operand(knext, m + NPK);
+            nxt[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[m >> 1], (m < 2) ? zero : nxt[m & 1], 0, 0, 0);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pb[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[st][8 * cc + e], c2, neg_m)));
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 pr = {pb[e], pb[e + 1]};
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lsum, false);
-                }
-                // A operand (32 head-dim rows x 16 keys) from two transposing
-                // reads: lane 16g + 4a + b addresses key 8*(g >> 1) + a (+4),
-                // columns 16*(g & 1) + 4b .. +3 of the row-major V tile.
-                const int row = 32 * st + 16 * cc + tr_row;
-                const char* rp = vt_lds + row * (2 * D) + tr_half;
-                const int sw = TL::vswz(row);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const char* p = rp + 16 * ((4 * dt + tr_lch) ^ sw);
-                    const short4_t lo = lds_read_tr(p);
-                    const short4_t hi = lds_read_tr(p + 4 * (2 * D));
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
-                }
+            for (int q = 0; q < PPM; ++q) {
+                const int p = m * PPM + q;          // pair p: chunk p / 4, elements 2*(p % 4), +1
+                const int c = p >> 2, e = 2 * (p & 3);
+                const float x0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + e], c2, neg_m));
+                const float x1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + e + 1], c2, neg_m));
+                const bf16x2 pr = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+                pb[c][e] = pr[0];
+                pb[c][e + 1] = pr[1];
+                lpart[p & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lpart[p & 1], false);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lsum += lpart[0] + lpart[1];
+        bf16x8 vb[NPV];
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) vb[i] = v_operand(vt_lds, i);
+        float mxp[2] = {-INFINITY, -INFINITY};  // two independent max chains
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < PVM; ++n) {
+            const bf16x8 va = vb[n % NPV];
+            if (n + NPV < PVM) vb[n % NPV] = v_operand(vt_lds, n + NPV);
+            oacc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n / DT], oacc[n % DT], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 16 / PVM; ++q) {    // two score registers per step
+                const int r = 2 * (n * (16 / PVM) + q);
+                const int ch = (n * (16 / PVM) + q) & 1;
+                mxp[ch] = fmaxf(mxp[ch], fmaxf(nxt[r >> 4][r & 15], nxt[r >> 4][(r & 15) + 1]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return pair_max(fmaxf(mxp[0], mxp[1]));
     };
 
     // ---- prologue: K0, V0, K1 in flight; S(0) ---------------------------------
     if (nt > 0) {
-        copy_tile(Kg, 0, k_off(0), true);
-        copy_tile(Vg, 0, v_off(0), false);
+        copy_tile(kp, 0, K_OFF0);
+        copy_tile(vp, 0, V_OFF0);
     }
-    if (nt > 1) copy_tile(Kg, 1, k_off(1), true);
+    if (nt > 1) copy_tile(kp, 1, K_OFF1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     f32x16 sA[2], sB[2];
-    if (wnt > 0) scores(sA, 0);
+    float mx_cur = -INFINITY;
+    if (wnt > 0) {
+        scores(sA, smem + K_OFF0);
+        if (needs_mask(0)) apply_mask(sA, 0);
+        mx_cur = tile_max(sA);
+    }
     __syncthreads();  // every wave is done with K0 before K2 overwrites it
 
-    // ---- main loop, unrolled by two so the score buffers alternate -----------
-    auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-        if (kt + 2 < nt) copy_tile(Kg, kt + 2, k_off(kt & 1), true);
-        if (kt + 1 < nt) copy_tile(Vg, kt + 1, v_off((kt + 1) & 1), false);
-        if (kt < wnt) softmax_pv(cur, kt, kt & 1, nxt, (kt + 1) & 1);
+    // ---- main loop, unrolled by two so buffers and score sets alternate ------
+    auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
+                    int v_cur_off, int v_nxt_off) {
+        if (kt + 2 < nt) copy_tile(kp, kt + 2, k_cur_off);
+        if (kt + 1 < nt) copy_tile(vp, kt + 1, v_nxt_off);
+        if (kt < wnt) {
+            advance_max(mx_cur);
+            mx_cur = main_block(cur, smem + v_cur_off, nxt, smem + k_nxt_off);
+            if (needs_mask(kt + 1)) {  // at most the diagonal and the ragged tile
+                apply_mask(nxt, kt + 1);
+                mx_cur = tile_max(nxt);
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
     for (int kt = 0; kt < nt; kt += 2) {
-        step(kt, sA, sB);
-        if (kt + 1 < nt) step(kt + 1, sB, sA);
+        step(kt, sA, sB, K_OFF0, K_OFF1, V_OFF0, V_OFF1);
+        if (kt + 1 < nt) step(kt + 1, sB, sA, K_OFF1, K_OFF0, V_OFF1, V_OFF0);
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
