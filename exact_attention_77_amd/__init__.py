@@ -5,8 +5,8 @@ kernels behind the C ABI declared in ``include/flash_attn.h``.  PyTorch is used
 for device memory and the current stream.  The functions carry the C names:
 
     flash_attn_fwd(q, k, v, causal=False, scale=None) -> (o, lse)
-    flash_attn_fp8_quantize(x, rotate, signs, block_rows) -> (x_fp8, scales)
-    flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal, scale) -> (o_bf16, lse)
+    flash_attn_fp8_quantize(x, role, rotate=False, signs=None) -> (x_fp8, scales)
+    flash_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale) -> (o_bf16, lse)
 
 If the shared library is missing this module raises on first use: there is no
 fallback path.
@@ -20,9 +20,10 @@ import threading
 
 __all__ = [
     "FlashAttnError", "lib_path", "load", "flash_attn_fwd", "flash_attn_fp8_quantize",
-    "flash_attn_fwd_fp8", "flash_attn_fp8_block_rows", "flash_attn_status_str",
-    "flash_attn_last_error", "flash_attn_abi_version", "Layout", "FwdOpts", "STATUS",
-    "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "EXPORTED_SYMBOLS",
+    "flash_attn_fwd_fp8", "flash_attn_fp8_buffer_bytes", "flash_attn_fp8_num_scales",
+    "flash_attn_status_str", "flash_attn_last_error", "flash_attn_abi_version", "Layout",
+    "FwdOpts", "STATUS", "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "ROLE_Q", "ROLE_K",
+    "ROLE_V", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,7 @@ _lock = threading.Lock()
 _lib = None
 
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+ROLE_Q, ROLE_K, ROLE_V = 0, 1, 2
 STATUS = {
     0: "FLASH_ATTN_OK", 1: "FLASH_ATTN_ERR_NULL", 2: "FLASH_ATTN_ERR_SHAPE",
     3: "FLASH_ATTN_ERR_LAYOUT", 4: "FLASH_ATTN_ERR_DTYPE", 5: "FLASH_ATTN_ERR_UNSUPPORTED",
@@ -38,9 +40,9 @@ STATUS = {
 }
 # Every function include/flash_attn.h declares.
 EXPORTED_SYMBOLS = (
-    "flash_attn_fwd", "flash_attn_fp8_quantize", "flash_attn_fp8_block_rows",
-    "flash_attn_fwd_fp8", "flash_attn_status_str", "flash_attn_last_error",
-    "flash_attn_abi_version",
+    "flash_attn_fwd", "flash_attn_fp8_quantize", "flash_attn_fp8_buffer_bytes",
+    "flash_attn_fp8_num_scales", "flash_attn_fwd_fp8", "flash_attn_status_str",
+    "flash_attn_last_error", "flash_attn_abi_version",
 )
 
 
@@ -80,10 +82,12 @@ def load():
         P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.flash_attn_fwd.argtypes = [P, P, P, P, P, Layout, I, I, F, P, P]
         lib.flash_attn_fwd.restype = I
-        lib.flash_attn_fp8_quantize.argtypes = [P, I, Layout, I, P, I, P, P, P]
+        lib.flash_attn_fp8_quantize.argtypes = [P, I, Layout, I, I, P, P, P, P]
         lib.flash_attn_fp8_quantize.restype = I
-        lib.flash_attn_fp8_block_rows.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
-        lib.flash_attn_fp8_block_rows.restype = None
+        lib.flash_attn_fp8_buffer_bytes.argtypes = [Layout, I]
+        lib.flash_attn_fp8_buffer_bytes.restype = ctypes.c_size_t
+        lib.flash_attn_fp8_num_scales.argtypes = [Layout, I]
+        lib.flash_attn_fp8_num_scales.restype = ctypes.c_int64
         lib.flash_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, Layout, I, F, P, P]
         lib.flash_attn_fwd_fp8.restype = I
         lib.flash_attn_status_str.argtypes = [I]
@@ -114,11 +118,12 @@ def flash_attn_abi_version() -> int:
     return int(load().flash_attn_abi_version())
 
 
-def flash_attn_fp8_block_rows():
-    """(rows per Q scale block, rows per K/V scale block) of the fp8 kernel."""
-    a, b = ctypes.c_int(), ctypes.c_int()
-    load().flash_attn_fp8_block_rows(ctypes.byref(a), ctypes.byref(b))
-    return a.value, b.value
+def flash_attn_fp8_buffer_bytes(layout: Layout, role: int) -> int:
+    return int(load().flash_attn_fp8_buffer_bytes(layout, int(role)))
+
+
+def flash_attn_fp8_num_scales(layout: Layout, role: int) -> int:
+    return int(load().flash_attn_fp8_num_scales(layout, int(role)))
 
 
 def _layout_of(t) -> Layout:
@@ -174,32 +179,38 @@ def flash_attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
-def flash_attn_fp8_quantize(x, rotate: bool, signs=None, block_rows: int | None = None):
-    """Rotate (optionally) and block-quantise x [B, H, N, d] (f32/bf16) to e4m3.
+def flash_attn_fp8_quantize(x, role: int, rotate: bool = False, signs=None):
+    """Rotate (optionally, Q/K) and block-quantise x [B, H, N, d] (f32/bf16) to e4m3.
 
-    Returns (x_fp8 uint8 contiguous [B, H, N, d], scales float32 [B, H, nblk]).
+    Returns (x_fp8, scales): uint8 [B, H, N, d] for Q/K, the transposed
+    [B, H, d, N_pad] for V; fp32 scales [B, H, n_blocks].
     """
     import torch
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise FlashAttnError(4, f"unsupported dtype {x.dtype}")
     B, H, N, d = x.shape
-    if block_rows is None:
-        block_rows = flash_attn_fp8_block_rows()[0]
-    nblk = (N + block_rows - 1) // block_rows
-    out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    lay = _layout_of(x)
+    nbytes = flash_attn_fp8_buffer_bytes(lay, role)
+    nsc = flash_attn_fp8_num_scales(lay, role)
+    if role == ROLE_V:
+        npad = (N + 63) // 64 * 64
+        out = torch.empty((B, H, d, npad), dtype=torch.uint8, device=x.device)
+    else:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    assert out.numel() == nbytes
+    nblk = nsc // max(B * H, 1) if B * H else 0
     scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
     sp = signs.data_ptr() if (rotate and signs is not None) else None
     dt = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
-    _check(load().flash_attn_fp8_quantize(x.data_ptr(), dt, _layout_of(x), int(bool(rotate)), sp,
-                                          int(block_rows), out.data_ptr(), scales.data_ptr(),
-                                          _stream()))
+    _check(load().flash_attn_fp8_quantize(x.data_ptr(), dt, lay, int(role), int(bool(rotate)), sp,
+                                          out.data_ptr(), scales.data_ptr(), _stream()))
     return out, scales
 
 
-def flash_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False,
                        scale: float | None = None, tau_log2: float | None = None,
                        tile_cfg: int = 0, out=None, lse=None):
-    """FP8 attention on e4m3 inputs with block scales -> (o bf16 [B, H, N, d], lse)."""
+    """FP8 attention on the pre-pass outputs -> (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
     import torch
     B, H, N, d = q8.shape
     if out is None:
@@ -208,10 +219,12 @@ def flash_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = Fal
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d) if d else 1.0
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or not t.is_contiguous() or t.shape != q8.shape:
-            raise FlashAttnError(3, "fp8 inputs must be contiguous uint8 [B, H, N, d]")
-    _check(load().flash_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(),
+    for t in (q8, k8, v8t):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise FlashAttnError(3, "fp8 inputs must be contiguous uint8 tensors")
+    if k8.shape != q8.shape or v8t.shape[:3] != (B, H, d):
+        raise FlashAttnError(2, "k8 must match q8; v8t must be [B, H, d, N_pad]")
+    _check(load().flash_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
                                      q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
                                      out.data_ptr(), lse.data_ptr(), _layout_of(out),
                                      int(bool(causal)), float(scale), _opts(tau_log2, tile_cfg),

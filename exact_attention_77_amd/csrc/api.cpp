@@ -115,14 +115,16 @@ flash_attn_status flash_attn_fwd(const void* q, const void* k, const void* v, vo
 }
 
 flash_attn_status flash_attn_fp8_quantize(const void* x, flash_attn_dtype in_dtype,
-                                          flash_attn_layout layout, int rotate,
-                                          const int8_t* signs, int block_rows,
+                                          flash_attn_layout layout, flash_attn_fp8_role role,
+                                          int rotate, const int8_t* signs,
                                           uint8_t* x_fp8, float* scales, void* stream) {
     flash_attn_status st = check_shape(layout);
     if (st != FLASH_ATTN_OK) return st;
     if (in_dtype != FLASH_ATTN_F32 && in_dtype != FLASH_ATTN_BF16) return FLASH_ATTN_ERR_DTYPE;
+    if (role != FLASH_ATTN_FP8_Q && role != FLASH_ATTN_FP8_K && role != FLASH_ATTN_FP8_V)
+        return FLASH_ATTN_ERR_ARG;
     if (rotate != 0 && rotate != 1) return FLASH_ATTN_ERR_ARG;
-    if (block_rows != fa::kFp8QBlock && block_rows != fa::kFp8KVBlock) return FLASH_ATTN_ERR_ARG;
+    if (rotate && role == FLASH_ATTN_FP8_V) return FLASH_ATTN_ERR_ARG;
     if (is_empty(layout)) return FLASH_ATTN_OK;
     if (!x || !x_fp8 || !scales || (rotate && !signs)) return FLASH_ATTN_ERR_NULL;
     const int64_t eb = (in_dtype == FLASH_ATTN_F32) ? 4 : 2;
@@ -136,17 +138,32 @@ flash_attn_status flash_attn_fp8_quantize(const void* x, flash_attn_dtype in_dty
     a.H = static_cast<int32_t>(layout.heads);
     a.N = static_cast<int32_t>(layout.seqlen);
     a.D = static_cast<int32_t>(layout.head_dim);
-    a.rotate = rotate; a.signs = signs; a.block_rows = block_rows;
+    a.role = static_cast<int32_t>(role);
+    a.rotate = rotate; a.signs = signs;
     a.out = x_fp8; a.scales = scales;
     return hip_status(fa::launch_fp8_quantize(a, stream));
 }
 
-void flash_attn_fp8_block_rows(int* q_block_rows, int* kv_block_rows) {
-    if (q_block_rows) *q_block_rows = fa::kFp8QBlock;
-    if (kv_block_rows) *kv_block_rows = fa::kFp8KVBlock;
+size_t flash_attn_fp8_buffer_bytes(flash_attn_layout layout, flash_attn_fp8_role role) {
+    if (layout.batch < 0 || layout.heads < 0 || layout.seqlen < 0 || layout.head_dim < 0) return 0;
+    if (role != FLASH_ATTN_FP8_Q && role != FLASH_ATTN_FP8_K && role != FLASH_ATTN_FP8_V) return 0;
+    const int64_t rows = (role == FLASH_ATTN_FP8_V) ? fa::fp8_npad(layout.seqlen) : layout.seqlen;
+    return static_cast<size_t>(layout.batch * layout.heads * rows * layout.head_dim);
 }
 
-flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+int64_t flash_attn_fp8_num_scales(flash_attn_layout layout, flash_attn_fp8_role role) {
+    if (layout.batch < 0 || layout.heads < 0 || layout.seqlen < 0) return 0;
+    int64_t blk;
+    switch (role) {
+        case FLASH_ATTN_FP8_Q: blk = fa::kFp8QBlock; break;
+        case FLASH_ATTN_FP8_K: blk = fa::kFp8KBlock; break;
+        case FLASH_ATTN_FP8_V: blk = fa::kFp8VBlock; break;
+        default: return 0;
+    }
+    return layout.batch * layout.heads * ((layout.seqlen + blk - 1) / blk);
+}
+
+flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                                      const float* q_scale, const float* k_scale,
                                      const float* v_scale, void* o, float* lse,
                                      flash_attn_layout o_layout, int causal, float scale,
@@ -159,15 +176,15 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
     int tile_cfg;
     if ((st = check_opts(opts, &tau, &tile_cfg)) != FLASH_ATTN_OK) return st;
     if (is_empty(o_layout)) return FLASH_ATTN_OK;
-    if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse)
+    if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o || !lse)
         return FLASH_ATTN_ERR_NULL;
     if ((st = check_strides(o_layout, 2)) != FLASH_ATTN_OK) return st;
-    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(q_scale) & 3u) ||
         (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u))
         return FLASH_ATTN_ERR_LAYOUT;
     fa::Fp8Args a;
-    a.q = q8; a.k = k8; a.v = v8; a.qs = q_scale; a.ks = k_scale; a.vs = v_scale;
+    a.q = q8; a.k = k8; a.vt = v8t; a.qs = q_scale; a.ks = k_scale; a.vs = v_scale;
     a.o = o; a.lse = lse;
     a.osb = o_layout.stride_b; a.osh = o_layout.stride_h; a.oss = o_layout.stride_s;
     a.B = static_cast<int32_t>(o_layout.batch);
@@ -175,7 +192,7 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
     a.N = static_cast<int32_t>(o_layout.seqlen);
     a.D = static_cast<int32_t>(o_layout.head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.tau = tau;
+    a.tau = fminf(tau, 0.5f);  // 256 * 2^tau must stay below 448
     a.causal = causal;
     a.tile_cfg = tile_cfg;
     return hip_status(fa::launch_fwd_fp8(a, stream));

@@ -1,9 +1,456 @@
-// fp8.hip -- placeholder until the fp8 pre-pass and attention kernels land.
+// fp8.hip -- FP8 (OCP e4m3fn) path for gfx950: block-quantising pre-pass with
+// incoherent processing, and attention on the fp8 matrix cores.
+//
+// Method ("FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+// Low-precision", sec. 技術 3): Q, K and V are quantised per block of rows with
+// one scale each, which a blockwise attention kernel applies at no extra
+// cost; before quantising, Q and K are multiplied by M = diag(+-1) H_d / sqrt(d)
+// (H_d a Sylvester Hadamard matrix) so that outliers spread over a row; M is
+// orthogonal, so (QM)(KM)^T = QK^T.  The attention itself is the tiled online
+// softmax of "FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析"
+// (sec. 5, 6.2, 8) with fp32 accumulation.
+//
+// gfx950 mapping:
+//  * pre-pass: one workgroup per (batch, head, row block); a row is spread over
+//    D/4 lanes (4 elements each); the fast Walsh-Hadamard transform does its
+//    two in-lane stages and log2(D/4) cross-lane stages with lane shuffles;
+//    conversion uses v_cvt_pk_fp8_f32 (round to nearest even) on values clamped
+//    to +-448, which gives the saturating e4m3fn encoding.  V is written
+//    transposed ([d][keys], padded to 64 keys) through an LDS tile, so the
+//    attention kernel's PV operand is a plain contiguous LDS read.
+//  * attention: like the bf16 kernel, a wave owns 32 queries and computes the
+//    transposed score tile S^T = K Q^T, now with v_mfma_scale_f32_32x32x64_f8f6f4
+//    (K = 64 fp8 per step).  K rows enter the product in an order that leaves,
+//    in lane half h, exactly keys 32h .. 32h+31 of the 64-key tile, so the
+//    packed fp8 probabilities are the B operand of O^T += V^T P^T directly.
+//    Q and K block scales fold into the exp2 constant (the Q block is the
+//    wave's 32 rows, the K block the 32 keys a lane half holds, so both are
+//    per-lane scalars); the V block scale is a power of two handed to the
+//    matrix core as its E8M0 A-operand scale.  Probabilities enter as e4m3(256 p); the row sum and O carry the
+//    same factor 256, which cancels in O / l and is removed from the LSE.
 #include <hip/hip_runtime.h>
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
 
 #include "internal.h"
 
 namespace fa {
-int launch_fp8_quantize(const QuantArgs&, void*) { return static_cast<int>(hipErrorNotSupported); }
-int launch_fwd_fp8(const Fp8Args&, void*) { return static_cast<int>(hipErrorNotSupported); }
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+
+constexpr int kQBlk = kFp8QBlock;  // 32 query rows per Q scale (a wave's rows)
+constexpr int kKBlk = kFp8KBlock;  // 32 key rows per K scale (one lane half)
+constexpr int kVBlk = kFp8VBlock;  // 64 key rows per V scale (= K/V tile)
+
+// ---------------------------------------------------------------------------
+// Pre-pass
+// ---------------------------------------------------------------------------
+
+// Two floats -> two e4m3fn bytes in the low (HI = false) or high half of `old`.
+template <bool HI>
+__device__ __forceinline__ int cvt2(float a, float b, int old) {
+    a = fminf(fmaxf(a, -448.f), 448.f);
+    b = fminf(fmaxf(b, -448.f), 448.f);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+template <int D, bool IN_BF16>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantArgs a) {
+    constexpr int LPR = D / 4;     // lanes per row
+    constexpr int RPW = 64 / LPR;  // rows per wave per pass
+    constexpr int RPP = 4 * RPW;   // rows per workgroup pass
+    constexpr int MAXP = kVBlk / RPP;  // the largest block
+    __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) uint8_t vt_tile[D * kVBlk];
+
+    const int blk_rows = (a.role == 0) ? kQBlk : (a.role == 1) ? kKBlk : kVBlk;
+    const int npass = blk_rows / RPP;
+    const int nblk = (a.N + blk_rows - 1) / blk_rows;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = 4 * (lane % LPR);
+    const int rsub = lane / LPR;
+    const int64_t xbase = int64_t(b) * a.sb + int64_t(h) * a.sh;
+
+    float sg[4] = {1.f, 1.f, 1.f, 1.f};
+    if (a.rotate)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sg[e] = static_cast<float>(a.signs[col + e]);
+    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
+
+    float v[MAXP][4];
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        const int row = blk * blk_rows + p * RPP + wave * RPW + rsub;
+        if (p < npass && row < a.N) {
+            const int64_t off = xbase + int64_t(row) * a.ss + col;
+            if (IN_BF16) {
+                const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.x) + off);
+                x[0] = __uint_as_float(r.x << 16); x[1] = __uint_as_float(r.x & 0xFFFF0000u);
+                x[2] = __uint_as_float(r.y << 16); x[3] = __uint_as_float(r.y & 0xFFFF0000u);
+            } else {
+                const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + off);
+                x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+            }
+        }
+        if (a.rotate) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= sg[e];
+            // Walsh-Hadamard butterflies: element index 4*(lane % LPR) + e.
+            float y0 = x[0] + x[1], y1 = x[0] - x[1], y2 = x[2] + x[3], y3 = x[2] - x[3];
+            x[0] = y0 + y2; x[1] = y1 + y3; x[2] = y0 - y2; x[3] = y1 - y3;
+#pragma unroll
+            for (int m = 1; m < LPR; m <<= 1) {
+                const bool upper = (lane & m) != 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float o = __shfl_xor(x[e], m, 64);
+                    x[e] = upper ? (o - x[e]) : (x[e] + o);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= inv_sqrt_d;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[p][e] = x[e];
+            amax = fmaxf(amax, fabsf(x[e]));
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float scale = (amax > 0.f) ? amax / 448.f : 1.f;
+    if (a.role == 2 && amax > 0.f) {  // power-of-two ceiling for V
+        int e;
+        const float m = frexpf(scale, &e);
+        scale = (m == 0.5f) ? scale : ldexpf(1.f, e);
+    }
+    if (tid == 0) a.scales[int64_t(bh) * nblk + blk] = scale;
+
+    if (a.role != 2) {
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const int row = blk * blk_rows + p * RPP + wave * RPW + rsub;
+            if (p < npass && row < a.N) {
+                int w = cvt2<false>(v[p][0] / scale, v[p][1] / scale, 0);
+                w = cvt2<true>(v[p][2] / scale, v[p][3] / scale, w);
+                *reinterpret_cast<int*>(a.out + (int64_t(bh) * a.N + row) * D + col) = w;
+            }
+        }
+        return;
+    }
+    // V: transpose through LDS, [d][64 keys] bytes, rows past N are zero.
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p < npass) {
+            const int r = p * RPP + wave * RPW + rsub;  // row inside the block
+            int w = cvt2<false>(v[p][0] / scale, v[p][1] / scale, 0);
+            w = cvt2<true>(v[p][2] / scale, v[p][3] / scale, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vt_tile[(col + e) * kVBlk + r] = static_cast<uint8_t>(w >> (8 * e));
+        }
+    }
+    __syncthreads();
+    const int64_t npad = fp8_npad(a.N);
+    for (int c = tid; c < D * kVBlk / 16; c += 256) {
+        const int d = c / (kVBlk / 16), part = c % (kVBlk / 16);
+        *reinterpret_cast<uint4*>(a.out + (int64_t(bh) * D + d) * npad + int64_t(blk) * kVBlk + 16 * part) =
+            *reinterpret_cast<const uint4*>(vt_tile + d * kVBlk + 16 * part);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention
+// ---------------------------------------------------------------------------
+
+constexpr int BC = kVBlk;   // keys per tile
+constexpr int WQ = 32;      // query rows per wave
+
+template <int D>
+struct Tile8 {
+    static constexpr int KBYTES = BC * D;          // K tile [64 keys][D] bytes
+    static constexpr int VBYTES = D * BC;          // V^T tile [D][64 keys] bytes
+    static constexpr int LDS_BYTES = 2 * KBYTES + 2 * VBYTES;
+    static constexpr int KCPR = D / 16;            // 16-byte chunks per K row
+    // K: the 16 rows read together are keys {0..7, 32..39} (+16 st); the
+    // swizzle gives each of them its own bank group.
+    __device__ static int kswz(int r) {
+        return D == 128 ? (((r >> 1) & 3) | (((r >> 5) & 1) << 2)) : (((r >> 2) & 1) | (((r >> 5) & 1) << 1));
+    }
+    // V^T: 16 consecutive head-dim rows of 64 bytes.
+    __device__ static int vswz(int r) { return (r >> 2) & 3; }
+};
+
+// A-operand row rho of score subtile st loads key
+//   32 * ((rho >> 2) & 1) + 16 * st + 4 * (rho >> 3) + (rho & 3)
+// so accumulator register g of subtile st in lane half h is key 32h + 16st + g.
+__device__ __forceinline__ int krow8(int rho, int st) {
+    return 32 * ((rho >> 2) & 1) + 16 * st + 4 * (rho >> 3) + (rho & 3);
+}
+
+__device__ __forceinline__ float pair_max8(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum8(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_fp8_kernel(Fp8Args a) {
+    using TL = Tile8<D>;
+    constexpr int BR = NW * WQ;
+    constexpr int KS = D / 64;   // k-steps of the score product
+    constexpr int DT = D / 32;   // head-dim tiles of O^T
+    constexpr int NBK = TL::KBYTES / 1024, NBV = TL::VBYTES / 1024;
+
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int n_qt = (a.N + BR - 1) / BR;
+    const int total = n_qt * a.B * a.H;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        id = (id & 7) * per + (id >> 3);
+    }
+    const int bh = id / n_qt;
+    int qt = id % n_qt;
+    if (CAUSAL) qt = n_qt - 1 - qt;
+    const int b = bh / a.H, h = bh % a.H;
+    const int64_t npad = fp8_npad(a.N);
+    const uint8_t* Qg = a.q + int64_t(bh) * a.N * D;
+    const uint8_t* Kg = a.k + int64_t(bh) * a.N * D;
+    const uint8_t* Vg = a.vt + int64_t(bh) * D * npad;
+    uint16_t* Og = static_cast<uint16_t*>(a.o) + int64_t(b) * a.osb + int64_t(h) * a.osh;
+    const int nqb = (a.N + kQBlk - 1) / kQBlk, nkb = (a.N + kKBlk - 1) / kKBlk;
+    const int nvb = (a.N + kVBlk - 1) / kVBlk;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int q0 = qt * BR + wave * WQ;
+    const int qi = q0 + j;
+
+    const int n_kt_all = (a.N + BC - 1) / BC;
+    const int nt = CAUSAL ? min(n_kt_all, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt_all;
+    int wnt = CAUSAL ? min(nt, (min(a.N, q0 + WQ) + BC - 1) / BC) : nt;
+    if (q0 >= a.N) wnt = 0;
+
+    // direct global -> LDS copies (1 KB per wave instruction, XOR-swizzled rows)
+    auto copy_k = [&](int kt, int off) {
+        for (int bk = wave; bk < NBK; bk += NW) {
+            const int c = bk * 64 + lane;
+            const int row = c / TL::KCPR, pch = c % TL::KCPR;
+            const int key = min(kt * BC + row, a.N - 1);
+            const uint8_t* g = Kg + int64_t(key) * D + 16 * (pch ^ TL::kswz(row));
+            __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
+        }
+    };
+    auto copy_v = [&](int kt, int off) {
+        for (int bk = wave; bk < NBV; bk += NW) {
+            const int c = bk * 64 + lane;
+            const int row = c / 4, pch = c % 4;  // row = head-dim index
+            const uint8_t* g = Vg + int64_t(row) * npad + int64_t(kt) * BC + 16 * (pch ^ TL::vswz(row));
+            __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
+        }
+    };
+    constexpr int K_OFF0 = 0, K_OFF1 = TL::KBYTES, V_OFF0 = 2 * TL::KBYTES, V_OFF1 = 2 * TL::KBYTES + TL::VBYTES;
+
+    // Q^T operand: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31]
+    i32x8 qreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+        if (qi < a.N) {
+            const uint8_t* p = Qg + int64_t(qi) * D + 64 * ks + 32 * hh;
+            lo = *reinterpret_cast<const uint4*>(p);
+            hi = *reinterpret_cast<const uint4*>(p + 16);
+        }
+        qreg[ks] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    }
+    const float sq = (q0 < a.N) ? a.qs[int64_t(bh) * nqb + q0 / kQBlk] : 1.f;
+    const float c2q = a.scale_log2 * sq;
+
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) oacc[dt][g] = 0.f;
+    float m_ref = -FLT_MAX;  // log2 units of the true scaled score
+    float lsum = 0.f;        // this lane's share of sum(256 p)
+
+    auto scores = [&](f32x16 (&s)[2], const char* kt_lds) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
+            const int row = krow8(j, st);
+            const char* rp = kt_lds + row * D;
+            const int sw = TL::kswz(row);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh) ^ sw));
+                const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh + 1) ^ sw));
+                const i32x8 ka = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+                s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qreg[ks], s[st], 0, 0, 0, 127, 0, 127);
+            }
+        }
+    };
+
+    auto softmax_pv = [&](f32x16 (&s)[2], int kt, const char* vt_lds, f32x16 (&nxt)[2], const char* knext) {
+        const int k_lo = kt * BC;
+        // lane half hh holds keys 32hh .. 32hh+31 of the tile: K block 2kt + hh
+        const int kb = min(2 * kt + hh, nkb - 1);
+        const float ct = c2q * a.ks[int64_t(bh) * nkb + kb];
+        const float sv = a.vs[int64_t(bh) * nvb + kt];
+        const int e8v = (__float_as_uint(sv) >> 23) & 0xFF;  // power of two -> E8M0
+        if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
+            const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 32 * hh;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int g = 0; g < 16; ++g)
+                    if (16 * st + g > lim) s[st][g] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) mx = fmaxf(mx, s[st][g]);
+        const float mt = pair_max8(mx * ct);
+        if (__any(mt > m_ref + a.tau)) {
+            const float mn = fmaxf(m_ref, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
+            m_ref = mn;
+        }
+        scores(nxt, knext);
+        const float bias = 8.f - m_ref;  // exp2(s*ct - m + 8) = 256 p
+        i32x8 pb;
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 0], ct, bias));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 1], ct, bias));
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 2], ct, bias));
+                const float p3 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 3], ct, bias));
+                ls0 += p0 + p1;
+                ls1 += p2 + p3;
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                pb[4 * st + r] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+            }
+        lsum += ls0 + ls1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int row = 32 * dt + j;
+            const char* rp = vt_lds + row * BC;
+            const int sw = TL::vswz(row);
+            const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh) ^ sw));
+            const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh + 1) ^ sw));
+            const i32x8 va = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[dt], 0, 0, 0, e8v, 0, 127);
+        }
+    };
+
+    if (nt > 0) {
+        copy_k(0, K_OFF0);
+        copy_v(0, V_OFF0);
+    }
+    if (nt > 1) copy_k(1, K_OFF1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 sA[2], sB[2];
+    if (wnt > 0) scores(sA, smem + K_OFF0);
+    __syncthreads();
+
+    auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
+                    int v_cur_off, int v_nxt_off) {
+        if (kt + 2 < nt) copy_k(kt + 2, k_cur_off);
+        if (kt + 1 < nt) copy_v(kt + 1, v_nxt_off);
+        if (kt < wnt) softmax_pv(cur, kt, smem + v_cur_off, nxt, smem + k_nxt_off);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    for (int kt = 0; kt < nt; kt += 2) {
+        step(kt, sA, sB, K_OFF0, K_OFF1, V_OFF0, V_OFF1);
+        if (kt + 1 < nt) step(kt + 1, sB, sA, K_OFF1, K_OFF0, V_OFF1, V_OFF0);
+    }
+
+    if (qi < a.N && wnt > 0) {
+        const float lt = pair_sum8(lsum);
+        const float inv = 1.0f / lt;
+        uint16_t* orow = Og + int64_t(qi) * a.oss;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                __bf16 o4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * r + t] * inv);
+                *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, o4);
+            }
+        if (hh == 0)
+            a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt) - 8.f) * 0.69314718055994531f;
+    }
+}
+
+template <int D, bool BF>
+int launch_q(const QuantArgs& a, hipStream_t s) {
+    const int blk_rows = (a.role == 0) ? kQBlk : (a.role == 1) ? kKBlk : kVBlk;
+    const int64_t grid = int64_t(a.B) * a.H * ((a.N + blk_rows - 1) / blk_rows);
+    hipLaunchKernelGGL((fp8_quantize_kernel<D, BF>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int D, bool CAUSAL>
+int launch_a(const Fp8Args& a, hipStream_t s) {
+    constexpr int NW = 8;
+    constexpr int LDS = Tile8<D>::LDS_BYTES;
+    auto kern = fwd_fp8_kernel<D, NW, CAUSAL>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+    }
+    const int n_qt = (a.N + NW * WQ - 1) / (NW * WQ);
+    const int64_t grid = int64_t(n_qt) * a.B * a.H;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), LDS, s, a);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_fp8_quantize(const QuantArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.D == 64) return a.in_bf16 ? launch_q<64, true>(a, s) : launch_q<64, false>(a, s);
+    return a.in_bf16 ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);
+}
+
+int launch_fwd_fp8(const Fp8Args& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.D == 64) return a.causal ? launch_a<64, true>(a, s) : launch_a<64, false>(a, s);
+    return a.causal ? launch_a<128, true>(a, s) : launch_a<128, false>(a, s);
+}
+
 }  // namespace fa

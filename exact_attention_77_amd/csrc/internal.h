@@ -26,18 +26,18 @@ struct QuantArgs {
     int32_t in_bf16;      // 1: x is bf16, 0: x is f32
     int64_t sb, sh, ss;   // strides of x (elements)
     int32_t B, H, N, D;
+    int32_t role;         // 0 Q, 1 K, 2 V
     int32_t rotate;
     const int8_t* signs;  // [D] +-1 (device)
-    int32_t block_rows;
-    uint8_t* out;         // contiguous [B, H, N, D]
-    float* scales;        // [B, H, ceil(N / block_rows)]
+    uint8_t* out;         // Q/K: [B, H, N, D]; V: [B, H, D, N_pad]
+    float* scales;        // [B, H, ceil(N / block)]
 };
 
 // FP8 attention arguments.
 struct Fp8Args {
     const uint8_t* q;
-    const uint8_t* k;
-    const uint8_t* v;      // contiguous [B, H, N, D]
+    const uint8_t* k;      // contiguous [B, H, N, D]
+    const uint8_t* vt;     // contiguous [B, H, D, N_pad]
     const float* qs;
     const float* ks;
     const float* vs;       // per-block scales
@@ -57,8 +57,12 @@ int launch_fwd_f32(const FwdArgs& a, void* stream);
 int launch_fp8_quantize(const QuantArgs& a, void* stream);
 int launch_fwd_fp8(const Fp8Args& a, void* stream);
 
-// Rows per scale block the fp8 attention kernel is built for.
-constexpr int kFp8QBlock = 128;
-constexpr int kFp8KVBlock = 64;
+// Rows per scale block the fp8 attention kernel is built for (Q: a wave's
+// 32 query rows; K: the 32 keys one lane half holds; V: one 64-key tile), and
+// the key padding of the transposed V buffer.
+constexpr int kFp8QBlock = 32;
+constexpr int kFp8KBlock = 32;
+constexpr int kFp8VBlock = 64;
+constexpr int64_t fp8_npad(int64_t n) { return (n + kFp8VBlock - 1) / kFp8VBlock * kFp8VBlock; }
 
 }  // namespace fa

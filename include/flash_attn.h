@@ -106,35 +106,53 @@ flash_attn_status flash_attn_fwd(const void* q, const void* k, const void* v,
  * and Low-precision", sec. 技術 3, accuracy part): optional incoherent
  * processing x -> (x * signs) H_d / sqrt(d) (Sylvester Hadamard H_d, applied as
  * a fast Walsh-Hadamard transform), then block quantisation: rows of one
- * (batch, head) are grouped in blocks of `block_rows` consecutive rows, each
- * block gets scale = amax(block) / 448 (1 for an all-zero block) and every
- * element becomes e4m3(x / scale) (round to nearest even, saturating at 448).
- *   x       : [layout] F32 or BF16 input (`in_dtype`)
- *   rotate  : 1 = apply the rotation (Q and K), 0 = none (V)
- *   signs   : device int8[head_dim] of +1/-1 (ignored when rotate == 0)
- *   block_rows : rows per scale block; must equal the value the fp8 attention
- *              kernel expects (flash_attn_fp8_block_rows)
- *   x_fp8   : output, contiguous [batch, heads, seqlen, head_dim] e4m3 bytes
- *   scales  : output, fp32 [batch, heads, ceil(seqlen / block_rows)]
+ * (batch, head) are grouped in blocks of consecutive rows, each block gets one
+ * fp32 scale and every element becomes e4m3(x / scale) (round to nearest even,
+ * saturating at +-448).  The role fixes the block size, the scale rule and the
+ * output layout the fp8 attention kernel consumes:
+ *   Q: blocks of 32 rows, scale = amax(block)/448 (1 for an all-zero block),
+ *      output contiguous [B, H, N, d];
+ *   K: blocks of 32 rows, same scale rule, output contiguous [B, H, N, d];
+ *   V: blocks of 64 rows, scale = the smallest power of two >= amax/448 (so the
+ *      matrix cores apply it as an exponent), never rotated, output TRANSPOSED
+ *      contiguous [B, H, d, N_pad] with N_pad = ceil(N / 64) * 64 (pad columns 0).
+ * Q and K must use the same signs (or both rotate = 0): the rotation is
+ * orthogonal, so Q K^T is unchanged and V needs no inverse rotation.
+ *   x      : [layout] F32 or BF16 input (`in_dtype`)
+ *   rotate : 1 = apply the rotation (Q, K only), 0 = none
+ *   signs  : device int8[head_dim] of +1/-1 (ignored when rotate == 0)
+ *   x_fp8  : output, flash_attn_fp8_buffer_bytes(layout, role) bytes
+ *   scales : output, fp32, flash_attn_fp8_num_scales(layout, role) entries,
+ *            [B, H, ceil(N / block)]
+ * Errors: as flash_attn_fwd, plus ERR_ARG for an unknown role or rotate on V.
  */
+typedef enum flash_attn_fp8_role {
+    FLASH_ATTN_FP8_Q = 0,
+    FLASH_ATTN_FP8_K = 1,
+    FLASH_ATTN_FP8_V = 2
+} flash_attn_fp8_role;
+
 flash_attn_status flash_attn_fp8_quantize(const void* x, flash_attn_dtype in_dtype,
-                                          flash_attn_layout layout, int rotate,
-                                          const int8_t* signs, int block_rows,
+                                          flash_attn_layout layout, flash_attn_fp8_role role,
+                                          int rotate, const int8_t* signs,
                                           uint8_t* x_fp8, float* scales, void* stream);
 
-/* Block sizes (rows per scale) that flash_attn_fwd_fp8 expects for Q and for K/V. */
-void flash_attn_fp8_block_rows(int* q_block_rows, int* kv_block_rows);
+/* Bytes of the e4m3 buffer and number of fp32 scales the pre-pass writes for a
+ * tensor of this shape and role (0 for an invalid role or negative sizes). */
+size_t flash_attn_fp8_buffer_bytes(flash_attn_layout layout, flash_attn_fp8_role role);
+int64_t flash_attn_fp8_num_scales(flash_attn_layout layout, flash_attn_fp8_role role);
 
 /*
- * FP8 forward attention: e4m3 Q, K, V (as written by flash_attn_fp8_quantize,
- * contiguous [batch, heads, seqlen, head_dim]) with their per-block fp32
- * scales; fp32 accumulation; O is bf16 with the strides of `o_layout`
- * (its batch/heads/seqlen/head_dim give the shape of everything).  Q and K
- * must have been rotated with the same signs (or both not rotated): the
- * rotation is orthogonal, so Q K^T is unchanged and V needs no inverse.
- * Probabilities enter the second product as e4m3 (scaled by 2^8).
+ * FP8 forward attention on the pre-pass outputs: e4m3 Q, K (contiguous
+ * [B, H, N, d]) and V (transposed [B, H, d, N_pad]) with their block scales;
+ * the matrix products run on the fp8 matrix cores with fp32 accumulation.  Q/K
+ * block scales fold into the softmax exponent, the power-of-two V scales are
+ * applied by the matrix cores, and the probabilities enter the second product
+ * as e4m3(256 p) (p <= 2^0.5: tau is capped at 0.5 here); the row sum uses the
+ * fp32 p.  O is bf16 with the strides of `o_layout`, whose batch, heads,
+ * seqlen and head_dim give the shape of everything; LSE is fp32 [B, H, N].
  */
-flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                                      const float* q_scale, const float* k_scale,
                                      const float* v_scale,
                                      void* o, float* lse, flash_attn_layout o_layout,

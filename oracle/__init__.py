@@ -69,7 +69,7 @@ def _load():
             lib.oracle_e4m3_encode.argtypes = [P, I, P]
             lib.oracle_e4m3_decode.argtypes = [P, I, P]
             lib.oracle_rotate_rows.argtypes = [P, I, I, P, P]
-            lib.oracle_quantize_blocks.argtypes = [P, I, I, I, I, P, P]
+            lib.oracle_quantize_blocks.argtypes = [P, I, I, I, I, ctypes.c_int, P, P]
             _lib = lib
     return _lib
 
@@ -183,14 +183,17 @@ def rotate(x, signs) -> np.ndarray:
     return out
 
 
-def quantize_blocks(x, block_rows: int):
-    """Per-block e4m3 quantisation of x [B, H, N, d] -> (codes uint8, scales [B, H, nblk])."""
+def quantize_blocks(x, block_rows: int, pow2: bool = False):
+    """Per-block e4m3 quantisation of x [B, H, N, d] -> (codes uint8, scales [B, H, nblk]).
+
+    scale = amax(block)/448, or its power-of-two ceiling when pow2 is set."""
     x = _f64(x)
     B, H, N, d = x.shape
     nblk = (N + block_rows - 1) // block_rows
     codes = np.empty(x.shape, np.uint8)
     scales = np.empty((B, H, nblk), np.float64)
-    _load().oracle_quantize_blocks(_ptr(x), B * H, N, d, int(block_rows), _ptr(codes), _ptr(scales))
+    _load().oracle_quantize_blocks(_ptr(x), B * H, N, d, int(block_rows), int(bool(pow2)),
+                                   _ptr(codes), _ptr(scales))
     return codes, scales
 
 

@@ -317,11 +317,19 @@ void oracle_rotate_rows(const double* x, int64_t rows, int64_t d,
 /*
  * Block quantisation ([FA3] sec. 技術 3): x is [BH, N, d]; rows are grouped in
  * blocks of block_rows consecutive rows of one (b, h) (the last block of a
- * head may be short).  scale = amax(block) / 448 (1 when amax is 0);
- * code = e4m3(x / scale).  scales: [BH, ceil(N / block_rows)].
+ * head may be short).  scale = amax(block) / 448 (1 when amax is 0), or with
+ * pow2 != 0 the smallest power of two >= amax(block) / 448 (a reading: the
+ * page fixes no scale format; a power of two lets hardware apply the scale
+ * as an exponent); code = e4m3(x / scale).  scales: [BH, ceil(N / block_rows)].
  */
+static double pow2_ceil(double t) {
+    int e;
+    const double m = frexp(t, &e);   /* t = m * 2^e, m in [0.5, 1) */
+    return (m == 0.5) ? t : ldexp(1.0, e);
+}
+
 void oracle_quantize_blocks(const double* x, int64_t BH, int64_t N, int64_t d,
-                            int64_t block_rows, uint8_t* codes, double* scales) {
+                            int64_t block_rows, int pow2, uint8_t* codes, double* scales) {
     const int64_t nblk = (N + block_rows - 1) / block_rows;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < BH * nblk; ++t) {
@@ -334,7 +342,8 @@ void oracle_quantize_blocks(const double* x, int64_t BH, int64_t N, int64_t d,
                 const double a = fabs(x[(bh * N + r) * d + c]);
                 if (a > amax) amax = a;
             }
-        const double sc = (amax > 0.0) ? amax / 448.0 : 1.0;
+        double sc = (amax > 0.0) ? amax / 448.0 : 1.0;
+        if (pow2 && amax > 0.0) sc = pow2_ceil(sc);
         scales[t] = sc;
         for (int64_t r = r0; r < r1; ++r)
             for (int64_t c = 0; c < d; ++c) {

@@ -33,7 +33,13 @@ def test_version_and_strings():
     assert fa.flash_attn_abi_version() == 1
     for code, name in fa.STATUS.items():
         assert fa.flash_attn_status_str(code) == name
-    assert fa.flash_attn_fp8_block_rows() == (128, 64)
+    lay = _lay(B=2, H=3, N=130, d=128)
+    assert fa.flash_attn_fp8_buffer_bytes(lay, fa.ROLE_Q) == 2 * 3 * 130 * 128
+    assert fa.flash_attn_fp8_buffer_bytes(lay, fa.ROLE_V) == 2 * 3 * 192 * 128   # padded to 64 keys
+    assert fa.flash_attn_fp8_num_scales(lay, fa.ROLE_Q) == 2 * 3 * 5
+    assert fa.flash_attn_fp8_num_scales(lay, fa.ROLE_K) == 2 * 3 * 5
+    assert fa.flash_attn_fp8_num_scales(lay, fa.ROLE_V) == 2 * 3 * 3
+    assert fa.flash_attn_fp8_num_scales(lay, 7) == 0
 
 
 def _lay(B=1, H=2, N=128, d=64, sb=None, sh=None, ss=None):
@@ -112,10 +118,11 @@ def test_f32_strides_need_16_bytes():
 def test_quantize_validation():
     lib = fa.load()
     lay = _lay()
-    assert lib.flash_attn_fp8_quantize(P, 1, lay, 1, None, 128, P, P, None) == 1
-    assert lib.flash_attn_fp8_quantize(P, 1, lay, 0, None, 100, P, P, None) == 6
-    assert lib.flash_attn_fp8_quantize(P, 2, lay, 0, None, 128, P, P, None) == 4
-    assert lib.flash_attn_fp8_quantize(None, 1, _lay(N=0), 0, None, 128, None, None, None) == 0
+    assert lib.flash_attn_fp8_quantize(P, 1, lay, fa.ROLE_Q, 1, None, P, P, None) == 1   # rotate needs signs
+    assert lib.flash_attn_fp8_quantize(P, 1, lay, 5, 0, None, P, P, None) == 6           # unknown role
+    assert lib.flash_attn_fp8_quantize(P, 1, lay, fa.ROLE_V, 1, P, P, P, None) == 6      # V is never rotated
+    assert lib.flash_attn_fp8_quantize(P, 2, lay, fa.ROLE_Q, 0, None, P, P, None) == 4
+    assert lib.flash_attn_fp8_quantize(None, 1, _lay(N=0), 0, 0, None, None, None, None) == 0
 
 
 def test_fp8_fwd_validation():

@@ -113,3 +113,21 @@ def test_per_tensor_baseline_is_worse_than_exact_on_outliers():
     o1, _ = oracle.fp8_per_tensor_baseline(q, k, v)
     rmse = np.sqrt(np.mean((o1 - o) ** 2))
     assert 1e-4 < rmse < 0.2
+
+
+def test_quantize_blocks_pow2_scales():
+    g = np.random.default_rng(3)
+    x = g.standard_normal((1, 1, 128, 8)) * np.array([1.0, 7.0, 0.01, 448.0 / 4])[None, None, :, None].repeat(32, 2).reshape(1, 1, 128, 1)
+    codes, scales = oracle.quantize_blocks(x, 32, pow2=True)
+    for b in range(4):
+        amax = np.max(np.abs(x[0, 0, 32 * b: 32 * b + 32]))
+        sc = scales[0, 0, b]
+        m, e = np.frexp(sc)
+        assert m == 0.5                               # a power of two
+        assert sc >= amax / 448.0 > sc / 2            # the smallest one above amax/448
+    vals = oracle.e4m3_decode(codes)
+    assert np.max(np.abs(vals)) <= 448.0
+    # a block whose amax/448 is exactly a power of two keeps that scale
+    y = np.zeros((1, 1, 4, 4)); y[0, 0, 0, 0] = 448.0 * 2.0 ** -3
+    _, s2 = oracle.quantize_blocks(y, 4, pow2=True)
+    assert s2[0, 0, 0] == 2.0 ** -3
