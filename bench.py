@@ -9,7 +9,7 @@ B=2 H=16 N=8192 d=128 forward.  Throughput is F / t with F = 4*B*H*N^2*d,
 halved when causal.  Prints ONE JSON line with a "roofline" object (achieved
 TFLOP/s of the kernel against the dense bf16 MFMA peak, timed with HIP events
 on the stream the kernel runs on) and a "cpu_baseline" object (the fp64 oracle
-timed on a bounded sample of rows of the same workload on the host cores).
+timed on a bounded sample of the same workload's heads on the host cores).
 """
 from __future__ import annotations
 
@@ -44,6 +44,22 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic(w):
+    """HBM bytes per launch recorded under profiles/ for this workload's kernel,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[w.name]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if sha != rec["source_sha256_16"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
+
 def cpu_baseline(w, target_s):
     """Time the fp64 oracle on a bounded, seeded sample of the workload: whole
     (batch, head) slices in a seeded order until about target_s of wall time."""
@@ -52,13 +68,16 @@ def cpu_baseline(w, target_s):
     import oracle
     from synth_inputs import normal_qkv, to_bf16
 
-    q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed)
+    q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
     order = np.random.Generator(np.random.PCG64(12345)).permutation(w.B * w.H)
     flops_per_head = w.flops / (w.B * w.H)
     done, t_total = 0, 0.0
     for bh in order:
         b, h = divmod(int(bh), w.H)
-        ref = [to_bf16(x[b:b + 1, h:h + 1])[1] for x in (q, k, v)]
+        if w.dtype == "bf16":
+            ref = [to_bf16(x[b:b + 1, h:h + 1])[1] for x in (q, k, v)]
+        else:
+            ref = [x[b:b + 1, h:h + 1] for x in (q, k, v)]
         t0 = time.perf_counter()
         oracle.attn_fwd(*ref, causal=w.causal)
         t_total += time.perf_counter() - t0
@@ -86,23 +105,51 @@ def main():
     from synth_inputs import WORKLOADS, normal_qkv, to_bf16
 
     w = WORKLOADS[args.workload]
-    if w.dtype not in ("bf16", "f32") or w.backward:
-        raise SystemExit(f"workload {w.name} is not a forward bf16/f32 workload")
+    if w.backward:
+        raise SystemExit(f"workload {w.name} is not a forward workload")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed)
-    if w.dtype == "bf16":
-        tens = [to_bf16(x)[0].to(dev) for x in (q, k, v)]
+    q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
+    extra = {}
+    if w.dtype == "fp8":
+        from synth_inputs import hadamard_signs
+        signs = torch.from_numpy(hadamard_signs(w.d)).to(dev)
+        xs = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+
+        def prepass():
+            q8, qs = fa.flash_attn_fp8_quantize(xs[0], fa.ROLE_Q, rotate=True, signs=signs)
+            k8, ks = fa.flash_attn_fp8_quantize(xs[1], fa.ROLE_K, rotate=True, signs=signs)
+            v8, vs = fa.flash_attn_fp8_quantize(xs[2], fa.ROLE_V)
+            return q8, k8, v8, qs, ks, vs
+        for _ in range(3):
+            prepass()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            f8 = prepass()
+        e1.record()
+        torch.cuda.synchronize()
+        extra["prepass_ms"] = round(e0.elapsed_time(e1) / 10, 5)
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+        del xs
     else:
-        tens = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+        if w.dtype == "bf16":
+            tens = [to_bf16(x)[0].to(dev) for x in (q, k, v)]
+        else:
+            tens = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+        o = torch.empty_like(tens[0])
     del q, k, v
-    o = torch.empty_like(tens[0])
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        fa.flash_attn_fwd(*tens, causal=w.causal, scale=w.scale, tile_cfg=args.tile_cfg,
-                          out=o, lse=lse)
+        if w.dtype == "fp8":
+            fa.flash_attn_fwd_fp8(*f8, causal=w.causal, scale=w.scale, tile_cfg=args.tile_cfg,
+                                  out=o, lse=lse)
+        else:
+            fa.flash_attn_fwd(*tens, causal=w.causal, scale=w.scale, tile_cfg=args.tile_cfg,
+                              out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -130,7 +177,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "bf16_causal_n8192_d128" else f"attention fwd TFLOP/s ({w.name})",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -141,15 +188,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1), bf16-rounded)",
+        "data": ("synthetic (seeded N(0,1), 0.1% x20 outliers, fp32 -> e4m3 pre-pass)"
+                 if w.dtype == "fp8" else "synthetic (seeded N(0,1), bf16-rounded)"),
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N,
                    "head_dim": w.d, "causal": w.causal, "scale": w.scale,
                    "flop_per_step": w.flops, "tile_cfg": args.tile_cfg},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
-                     "traffic": None, "kernel_ms": round(ms_ev, 5)},
+                     "traffic": measured_traffic(w), "kernel_ms": round(ms_ev, 5)},
     }
+    out.update(extra)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
