@@ -10,6 +10,11 @@ halved when causal.  Prints ONE JSON line with a "roofline" object (achieved
 TFLOP/s of the kernel against the dense bf16 MFMA peak, timed with HIP events
 on the stream the kernel runs on) and a "cpu_baseline" object (the fp64 oracle
 timed on a bounded sample of the same workload's heads on the host cores).
+
+The default warm-up (300 launches, about 0.2 s of back-to-back work for the
+headline workload) is there because the chip's clock settles only after tens
+of milliseconds of sustained MFMA load: launches in the first ~50 ms run up to
+20% slower than the steady state that the timed 200 launches then measure.
 """
 from __future__ import annotations
 
@@ -31,8 +36,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}   # MI355X dense, pu
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="bf16_causal_n8192_d128")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")

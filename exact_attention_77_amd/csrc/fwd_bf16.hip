@@ -338,7 +338,7 @@ void fwd_bf16_kernel(FwdArgs a) {
             for (int q = 0; q < 16 / PVM; ++q) {    // two score registers per step
                 const int r = 2 * (n * (16 / PVM) + q);
                 const int ch = (n * (16 / PVM) + q) & 1;
-                mxp[ch] = fmaxf(mxp[ch], fmaxf(nxt[r >> 4][r & 15], nxt[r >> 4][(r & 15) + 1]));
+                mxp[ch] = fmaxf(fmaxf(mxp[ch], nxt[r >> 4][r & 15]), nxt[r >> 4][(r & 15) + 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
