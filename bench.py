@@ -73,7 +73,10 @@ def cpu_baseline(w, target_s):
     import oracle
     from synth_inputs import normal_qkv, to_bf16
 
-    q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
+    if w.backward:
+        q, k, v, dout = normal_qkv(w.B, w.H, w.N, w.d, w.seed, with_dout=True)
+    else:
+        q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
     order = np.random.Generator(np.random.PCG64(12345)).permutation(w.B * w.H)
     flops_per_head = w.flops / (w.B * w.H)
     done, t_total = 0, 0.0
@@ -84,7 +87,10 @@ def cpu_baseline(w, target_s):
         else:
             ref = [x[b:b + 1, h:h + 1] for x in (q, k, v)]
         t0 = time.perf_counter()
-        oracle.attn_fwd(*ref, causal=w.causal)
+        if w.backward:
+            oracle.attn_bwd(*ref, to_bf16(dout[b:b + 1, h:h + 1])[1], causal=w.causal)
+        else:
+            oracle.attn_fwd(*ref, causal=w.causal)
         t_total += time.perf_counter() - t0
         done += 1
         if t_total >= target_s:
@@ -92,7 +98,8 @@ def cpu_baseline(w, target_s):
     return {"value": done * flops_per_head / t_total / 1e12, "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(t_total, 3),
             "sample": f"{done} of {w.B * w.H} (batch, head) slices of the workload, every row, "
-                      "fp64 two-pass, OpenMP over rows"}
+                      + ("fp64 analytic gradient, OpenMP over rows" if w.backward
+                         else "fp64 two-pass, OpenMP over rows")}
 
 
 def main():
@@ -110,11 +117,13 @@ def main():
     from synth_inputs import WORKLOADS, normal_qkv, to_bf16
 
     w = WORKLOADS[args.workload]
-    if w.backward:
-        raise SystemExit(f"workload {w.name} is not a forward workload")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
+    if w.backward:
+        q, k, v, dout = normal_qkv(w.B, w.H, w.N, w.d, w.seed, with_dout=True)
+        dout = to_bf16(dout)[0].to(dev)
+    else:
+        q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
     extra = {}
     if w.dtype == "fp8":
         from synth_inputs import hadamard_signs
@@ -148,8 +157,17 @@ def main():
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    if w.backward:  # O and LSE of the forward feed every backward step
+        fa.flash_attn_fwd(*tens, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        grads = [torch.empty_like(tens[0]) for _ in range(3)]
+        lay = fa.Layout(w.B, w.H, w.N, w.d, *tens[0].stride()[:3])
+        ws = torch.empty(fa.flash_attn_bwd_workspace_size(lay), dtype=torch.uint8, device=dev)
+
     def step():
-        if w.dtype == "fp8":
+        if w.backward:
+            fa.flash_attn_bwd(*tens, o, lse, dout, causal=w.causal, scale=w.scale,
+                              dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
+        elif w.dtype == "fp8":
             fa.flash_attn_fwd_fp8(*f8, causal=w.causal, scale=w.scale, tile_cfg=args.tile_cfg,
                                   out=o, lse=lse)
         else:
@@ -182,7 +200,8 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
 
     out = {
-        "metric": METRIC if w.name == "bf16_causal_n8192_d128" else f"attention fwd TFLOP/s ({w.name})",
+        "metric": METRIC if w.name == "bf16_causal_n8192_d128" else
+                  f"attention {'bwd' if w.backward else 'fwd'} TFLOP/s ({w.name})",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

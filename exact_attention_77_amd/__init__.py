@@ -7,6 +7,7 @@ for device memory and the current stream.  The functions carry the C names:
     flash_attn_fwd(q, k, v, causal=False, scale=None) -> (o, lse)
     flash_attn_fp8_quantize(x, role, rotate=False, signs=None) -> (x_fp8, scales)
     flash_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale) -> (o_bf16, lse)
+    flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
 
 If the shared library is missing this module raises on first use: there is no
 fallback path.
@@ -21,6 +22,7 @@ import threading
 __all__ = [
     "FlashAttnError", "lib_path", "load", "flash_attn_fwd", "flash_attn_fp8_quantize",
     "flash_attn_fwd_fp8", "flash_attn_fp8_buffer_bytes", "flash_attn_fp8_num_scales",
+    "flash_attn_bwd", "flash_attn_bwd_workspace_size",
     "flash_attn_status_str", "flash_attn_last_error", "flash_attn_abi_version", "Layout",
     "FwdOpts", "STATUS", "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "ROLE_Q", "ROLE_K",
     "ROLE_V", "EXPORTED_SYMBOLS",
@@ -41,8 +43,9 @@ STATUS = {
 # Every function include/flash_attn.h declares.
 EXPORTED_SYMBOLS = (
     "flash_attn_fwd", "flash_attn_fp8_quantize", "flash_attn_fp8_buffer_bytes",
-    "flash_attn_fp8_num_scales", "flash_attn_fwd_fp8", "flash_attn_status_str",
-    "flash_attn_last_error", "flash_attn_abi_version",
+    "flash_attn_fp8_num_scales", "flash_attn_fwd_fp8", "flash_attn_bwd",
+    "flash_attn_bwd_workspace_size", "flash_attn_status_str", "flash_attn_last_error",
+    "flash_attn_abi_version",
 )
 
 
@@ -90,6 +93,11 @@ def load():
         lib.flash_attn_fp8_num_scales.restype = ctypes.c_int64
         lib.flash_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, Layout, I, F, P, P]
         lib.flash_attn_fwd_fp8.restype = I
+        lib.flash_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, Layout, I, I, F, P,
+                                       ctypes.c_size_t, P]
+        lib.flash_attn_bwd.restype = I
+        lib.flash_attn_bwd_workspace_size.argtypes = [Layout, I]
+        lib.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.flash_attn_status_str.argtypes = [I]
         lib.flash_attn_status_str.restype = ctypes.c_char_p
         lib.flash_attn_last_error.argtypes = []
@@ -230,3 +238,48 @@ def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = Fa
                                      int(bool(causal)), float(scale), _opts(tau_log2, tile_cfg),
                                      _stream()))
     return out, lse
+
+
+def flash_attn_bwd_workspace_size(layout: Layout, dtype: int = DTYPE_BF16) -> int:
+    return int(load().flash_attn_bwd_workspace_size(layout, int(dtype)))
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                   dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of the bf16 forward for the upstream gradient dout.
+
+    q, k, v, o, dout: bfloat16 CUDA tensors [B, H, N, d] sharing shape and
+    strides (o and lse are the forward's outputs); lse: float32 [B, H, N].
+    The fp32 workspace is allocated here unless given (uint8 tensor of at least
+    flash_attn_bwd_workspace_size bytes).
+    """
+    import torch
+    ts = (q, k, v, o, dout)
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise FlashAttnError(4, "the backward takes bfloat16 q, k, v, o, dout")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise FlashAttnError(2, "q, k, v, o, dout must share a [B, H, N, d] shape")
+    if any(t.stride() != q.stride() for t in ts):
+        raise FlashAttnError(3, "q, k, v, o, dout must share strides")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise FlashAttnError(3, "lse must be a contiguous float32 [B, H, N] tensor")
+    lay = _layout_of(q)
+    outs = []
+    for t in (dq, dk, dv):
+        if t is None:
+            t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        elif t.stride() != q.stride() or t.shape != q.shape or t.dtype != q.dtype:
+            raise FlashAttnError(3, "gradient outputs must match q's shape, dtype and strides")
+        outs.append(t)
+    need = flash_attn_bwd_workspace_size(lay, DTYPE_BF16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d else 1.0
+    _check(load().flash_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), dout.data_ptr(), outs[0].data_ptr(),
+                                 outs[1].data_ptr(), outs[2].data_ptr(), lay, DTYPE_BF16,
+                                 int(bool(causal)), float(scale), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream()))
+    return tuple(outs)

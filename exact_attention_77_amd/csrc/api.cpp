@@ -198,6 +198,56 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
     return hip_status(fa::launch_fwd_fp8(a, stream));
 }
 
+size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype dtype) {
+    if (check_shape(layout) != FLASH_ATTN_OK || dtype != FLASH_ATTN_BF16) return 0;
+    if (is_empty(layout)) return 0;
+    return static_cast<size_t>(
+        fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen, layout.head_dim));
+}
+
+flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                 flash_attn_layout layout, flash_attn_dtype dtype, int causal,
+                                 float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    flash_attn_status st = check_shape(layout);
+    if (st != FLASH_ATTN_OK) return st;
+    if (dtype == FLASH_ATTN_F32) return FLASH_ATTN_ERR_UNSUPPORTED;
+    if (dtype != FLASH_ATTN_BF16) return FLASH_ATTN_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return FLASH_ATTN_ERR_ARG;
+    if ((st = check_scale(scale)) != FLASH_ATTN_OK) return st;
+    if (is_empty(layout)) return FLASH_ATTN_OK;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FLASH_ATTN_ERR_NULL;
+    if ((st = check_strides(layout, 2)) != FLASH_ATTN_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return FLASH_ATTN_ERR_LAYOUT;
+    const int64_t need = fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen,
+                                                 layout.head_dim);
+    if (!workspace || workspace_bytes < static_cast<size_t>(need) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return FLASH_ATTN_ERR_WORKSPACE;
+    fa::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.sb = layout.stride_b; a.sh = layout.stride_h; a.ss = layout.stride_s;
+    a.B = static_cast<int32_t>(layout.batch);
+    a.H = static_cast<int32_t>(layout.heads);
+    a.N = static_cast<int32_t>(layout.seqlen);
+    a.D = static_cast<int32_t>(layout.head_dim);
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.causal = causal;
+    char* ws = static_cast<char*>(workspace);
+    const int64_t rows = layout.batch * layout.heads * layout.seqlen;
+    a.ws_dq = reinterpret_cast<float*>(ws);
+    a.ws_lse2 = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows * layout.head_dim));
+    a.ws_nd = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows * layout.head_dim) +
+                                       fa::bwd_ws_part(rows));
+    return hip_status(fa::launch_bwd_bf16(a, stream));
+}
+
 const char* flash_attn_status_str(flash_attn_status s) {
     switch (s) {
         case FLASH_ATTN_OK: return "FLASH_ATTN_OK";

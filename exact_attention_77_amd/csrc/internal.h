@@ -51,11 +51,40 @@ struct Fp8Args {
     int32_t tile_cfg;
 };
 
+// Backward arguments (bf16 tensors sharing one layout; fp32 workspace split
+// into the dQ accumulator [B, H, N, D] and two per-row arrays [B, H, N]).
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;     // contiguous [B, H, N], natural log
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t sb, sh, ss;   // element strides shared by every tensor above
+    int32_t B, H, N, D;
+    float scale;
+    float scale_log2;
+    int32_t causal;
+    float* ws_dq;         // [B, H, N, D] fp32 accumulator
+    float* ws_lse2;       // [B, H, N] LSE * log2(e)
+    float* ws_nd;         // [B, H, N] -rowsum(dO o O)
+};
+
+// Workspace bytes of the backward pass (each part 256-byte aligned).
+inline int64_t bwd_ws_part(int64_t n) { return (n * 4 + 255) / 256 * 256; }
+inline int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
+    return bwd_ws_part(B * H * N * D) + 2 * bwd_ws_part(B * H * N);
+}
+
 // Launchers: return a hipError_t value (0 = success).
 int launch_fwd_bf16(const FwdArgs& a, void* stream);
 int launch_fwd_f32(const FwdArgs& a, void* stream);
 int launch_fp8_quantize(const QuantArgs& a, void* stream);
 int launch_fwd_fp8(const Fp8Args& a, void* stream);
+int launch_bwd_bf16(const BwdArgs& a, void* stream);
 
 // Rows per scale block the fp8 attention kernel is built for (Q: a wave's
 // 32 query rows; K: the 32 keys one lane half holds; V: one 64-key tile), and

@@ -159,6 +159,42 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
                                      int causal, float scale,
                                      const flash_attn_fwd_opts* opts, void* stream);
 
+/*
+ * Backward pass, bf16.  Gradients of the forward above with respect to Q, K
+ * and V for the upstream gradient dO.  The pages give no backward formulas;
+ * this is the analytic derivative of the definition (s = scale Q K^T, P =
+ * softmax(s) per row, P_ij = exp(s_ij - LSE_i)):
+ *     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P o (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ * As in "FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析"
+ * sec. 7.2, S and P are recomputed tile by tile on chip from Q, K and the
+ * forward's LSE; nothing N x N is stored.  Probabilities and dS enter the
+ * matrix products as bf16, accumulation is fp32.
+ *   q, k, v, o, dout : [layout] bf16 (o and lse are the forward's outputs)
+ *   lse              : fp32 [batch, heads, seqlen] from flash_attn_fwd
+ *   dq, dk, dv       : [layout] bf16 outputs (rounded to nearest even)
+ *   causal, scale    : as given to the forward
+ *   workspace        : device memory of at least
+ *                      flash_attn_bwd_workspace_size(layout, dtype) bytes,
+ *                      256-byte aligned, owned by the caller; its contents on
+ *                      entry do not matter and are overwritten (dQ is
+ *                      accumulated there in fp32 with atomic adds, so the
+ *                      summation order of dQ, and its last bits, can vary
+ *                      from call to call; dK and dV are deterministic).
+ * Errors: as flash_attn_fwd; dtype F32 -> ERR_UNSUPPORTED (bf16 only);
+ * workspace NULL, too small or misaligned -> ERR_WORKSPACE.
+ */
+flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout,
+                                 void* dq, void* dk, void* dv,
+                                 flash_attn_layout layout, flash_attn_dtype dtype,
+                                 int causal, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes flash_attn_bwd needs for this shape and dtype (0 for an
+ * empty shape, an invalid one or a dtype the backward does not accept). */
+size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype dtype);
+
 /* Human-readable name of a status code (static string). */
 const char* flash_attn_status_str(flash_attn_status s);
 

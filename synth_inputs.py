@@ -41,8 +41,9 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """Forward FLOPs 4*B*H*N^2*d, halved when causal."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        """Forward FLOPs 4*B*H*N^2*d (two products); a backward workload counts
+        10*B*H*N^2*d (five products: S, dP, dV, dK, dQ); halved when causal."""
+        f = (10.0 if self.backward else 4.0) * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
 

@@ -138,3 +138,39 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_lib", None)
     with pytest.raises(fa.FlashAttnError):
         fa.load()
+
+
+def bwd(lay=None, dtype=fa.DTYPE_BF16, causal=0, scale=0.125, ws=P, ws_bytes=1 << 40, **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv")}
+    p.update(ptrs)
+    return fa.load().flash_attn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"],
+                                    p["dk"], p["dv"], lay or _lay(), dtype, causal, scale, ws,
+                                    ws_bytes, None)
+
+
+def test_bwd_workspace_size():
+    lay = _lay(B=2, H=3, N=130, d=128)
+    rows = 2 * 3 * 130
+    part = lambda n: (4 * n + 255) // 256 * 256
+    assert fa.flash_attn_bwd_workspace_size(lay) == part(rows * 128) + 2 * part(rows)
+    assert fa.flash_attn_bwd_workspace_size(lay, fa.DTYPE_F32) == 0
+    assert fa.flash_attn_bwd_workspace_size(_lay(N=0)) == 0
+    assert fa.flash_attn_bwd_workspace_size(_lay(d=96)) == 0
+
+
+def test_bwd_validation():
+    for name in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"):
+        assert bwd(**{name: None}) == 1, name
+    assert bwd(dtype=fa.DTYPE_F32) == 5
+    assert bwd(dtype=fa.DTYPE_FP8_E4M3) == 4
+    assert bwd(causal=2) == 6
+    assert bwd(scale=float("nan")) == 6
+    assert bwd(lay=_lay(d=80)) == 5
+    assert bwd(lay=_lay(ss=60)) == 3
+    assert bwd(dq=P + 2) == 3
+    need = fa.flash_attn_bwd_workspace_size(_lay())
+    assert bwd(ws=None) == 7
+    assert bwd(ws_bytes=need - 1) == 7
+    assert bwd(ws=P + 16, ws_bytes=need) == 7
+    assert bwd(lay=_lay(N=0), ws=None, ws_bytes=0, **{n: None for n in ("q", "k", "v", "o", "lse",
+                                                                      "dout", "dq", "dk", "dv")}) == 0
