@@ -202,7 +202,7 @@ size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype 
     if (check_shape(layout) != FLASH_ATTN_OK || dtype != FLASH_ATTN_BF16) return 0;
     if (is_empty(layout)) return 0;
     return static_cast<size_t>(
-        fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen, layout.head_dim));
+        fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen));
 }
 
 flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -223,8 +223,7 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u))
         return FLASH_ATTN_ERR_LAYOUT;
-    const int64_t need = fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen,
-                                                 layout.head_dim);
+    const int64_t need = fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen);
     if (!workspace || workspace_bytes < static_cast<size_t>(need) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return FLASH_ATTN_ERR_WORKSPACE;
@@ -241,10 +240,8 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
     a.causal = causal;
     char* ws = static_cast<char*>(workspace);
     const int64_t rows = layout.batch * layout.heads * layout.seqlen;
-    a.ws_dq = reinterpret_cast<float*>(ws);
-    a.ws_lse2 = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows * layout.head_dim));
-    a.ws_nd = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows * layout.head_dim) +
-                                       fa::bwd_ws_part(rows));
+    a.ws_lse2 = reinterpret_cast<float*>(ws);
+    a.ws_nd = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows));
     return hip_status(fa::launch_bwd_bf16(a, stream));
 }
 

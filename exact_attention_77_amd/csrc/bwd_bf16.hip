@@ -13,33 +13,39 @@
 // P_ij = exp(s_ij - LSE_i)).
 //
 // Three kernels, all on the caller's stream:
-//  1. prep   : per query row, -D_i and LSE_i * log2(e) (fp32) into the
-//              workspace, and zeroes that row of the fp32 dQ accumulator.
-//  2. main   : one workgroup per (batch, head, 128-key tile), four waves of 32
-//              keys.  A wave keeps its K and V rows (as MFMA B operands) and
-//              its dK^T / dV^T accumulators in registers for the whole kernel
-//              and walks over 32-query tiles of Q and dO that the workgroup
-//              stages in LDS (direct global->LDS loads, double-buffered).  Per
-//              query tile, with v_mfma_f32_32x32x16_bf16:
-//                S = Q K^T and dP - D (the accumulator starts at -D); in the
-//                32x32 accumulator layout a lane holds ONE key and 16 queries;
-//                P = exp2(S * scale*log2e - LSE*log2e) -> bf16;
-//                dV^T += dO^T P and, with dS = P (dP - D) -> bf16,
-//                dK^T += Q^T dS.  Q rows enter the first products in a
-//                permuted order (bits 2 and 3 of the row swapped) so that the
-//                accumulator registers of P and dS are directly the B
-//                operands of these two products (no LDS round trip);
-//                dO^T and Q^T come from transposing LDS reads.
-//              dS^T then goes to LDS, and wave w forms dQ[:, 32w .. 32w+31]
-//              = dS K over the workgroup's 128 keys and adds it to the fp32
-//              accumulator with global float atomics.
-//  3. convert: dQ = bf16(scale * accumulator) in the caller's layout.
-// Workgroups run key tile 0 (the most queries under the causal mask) first,
+//  1. prep : per query row, -D_i and LSE_i * log2(e) (fp32) into the workspace.
+//  2. dK/dV: one workgroup per (batch, head, 128-key tile), eight waves; wave
+//            w works on key block w % 4 (32 keys) and query half w / 4 of each
+//            64-query tile of Q and dO, staged in LDS by direct global->LDS
+//            loads (double-buffered).  Per tile, with v_mfma_f32_32x32x16_bf16:
+//              S = Q K^T and dP - D (the accumulator starts at -D); in the
+//              32x32 accumulator layout a lane holds ONE key and 16 queries;
+//              P = exp2(S * scale*log2e - LSE*log2e), dS = P (dP - D) -> bf16,
+//              both stored transposed (row = key) to LDS;
+//              then the wave of query half 0 accumulates dV^T += dO^T P and
+//              the one of half 1 dK^T += Q^T dS over the whole 64-query tile
+//              (dO^T, Q^T by transposing LDS reads; P^T, dS^T by row reads).
+//  3. dQ   : one workgroup per (batch, head, 256-query tile), eight waves of
+//            32 queries, K/V tiles of 64 keys streamed through LDS (the loop
+//            order of the forward pass).  Per tile the transposed products
+//            S^T = K Q^T and dP^T - D = V dO^T (Q^T, dO^T held in registers)
+//            put one query per lane, dS^T = P^T (dP^T - D) -> bf16 is, with K
+//            rows fed in a permuted order, directly the B operand of
+//            dQ^T += K^T dS^T, and dQ is written once at the end.
+// dQ is thus computed by recomputing S and dP per query tile instead of being
+// summed over key tiles with atomic adds: 40% more matrix work, but the fp32
+// atomics into a shared accumulator cost more than that on this chip (their
+// throughput at the L2 is far below the matrix cores'), and the result is
+// deterministic.  "FlashAttention-4" (abstract) likewise names the atomic
+// adds of the backward pass as a cost to cut.
+// Workgroups run the tiles with the most work first under the causal mask,
 // and the tiles of one head share an XCD (ids are dealt round-robin over the
-// 8 XCDs), so a head's Q/dO stream stays in one L2.
+// 8 XCDs), so that head's K/V or Q/dO stream stays in one L2.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -57,6 +63,9 @@ typedef __attribute__((address_space(1))) const void global_cvoid;
 constexpr int BK = 128;  // keys per workgroup (32 per wave)
 constexpr int BQ = 64;   // queries per tile of the inner loop (32 per wave)
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate for lgkmcnt(0) alone (gfx9 encoding: vmcnt bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int kWaitLds = 0xC07F;
 
 // XOR swizzle (16-byte chunk units) of a row of a Q, dO or K tile in LDS.  A
 // tile is read two ways: by rows (16 lanes read one chunk of 16 rows) and
@@ -86,7 +95,8 @@ __device__ __forceinline__ bf16x8 cat(short4_t lo, short4_t hi) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. prep: D/8 lanes per query row.
+// 1. prep: D/8 lanes per query row.  -D and LSE*log2e are what the two main
+// kernels add to their score accumulators.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     constexpr int LPR = D / 8;
@@ -107,9 +117,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(o8[e]), static_cast<float>(g8[e]), acc);
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, LPR);
-    float4* z = reinterpret_cast<float4*>(a.ws_dq + row * D + 8 * l);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (l == 0) {
         a.ws_nd[row] = -acc;
         a.ws_lse2[row] = a.lse[row] * kLog2e;
@@ -117,12 +124,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. main kernel: 8 waves; wave w works on key block kb = w % 4 (32 keys) and
+// 2. dK/dV kernel: 8 waves; wave w works on key block kb = w % 4 (32 keys) and
 // query half qh = w / 4 (32 of the tile's 64 queries) for S, dP, P and dS; the
 // wave with qh = 0 accumulates dV of its key block, the one with qh = 1 dK.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_bf16_kernel(BwdArgs a) {
+void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int KS = D / 16;          // k-steps over the head dim
     constexpr int DT = D / 32;          // 32-column head-dim tiles
     constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -131,18 +138,18 @@ void bwd_bf16_kernel(BwdArgs a) {
     constexpr int NQB = BQ * CPR / 64 / 8;   // 1 KB copy blocks per wave, Q (and dO) tile
     constexpr int NKB = BK * CPR / 64 / 8;   // 1 KB copy blocks per wave, K tile
     constexpr int PT_BYTES = BK * BQ * 2;    // P^T or dS^T: [128 keys][64 queries] bf16
-    constexpr int OFF_K = 0;
-    constexpr int OFF_Q = OFF_K + KT_BYTES;
-    constexpr int OFF_O = OFF_Q + 2 * QT_BYTES;
-    constexpr int OFF_L = OFF_O + 2 * QT_BYTES;   // per buffer: 64 lse2 then 64 -D
-    constexpr int OFF_P = OFF_L + 2 * 512;
-    constexpr int OFF_S = OFF_P + PT_BYTES;
-    // dQ: 2 query halves x DT head-dim tiles, each over BK keys; with DT < 4
-    // two waves split the keys of one output tile.
-    constexpr int DQ_KSTEPS = BK / 16 * DT / 4;
-    static_assert(NQB >= 1 && NKB >= 1 && DQ_KSTEPS >= 2, "tile shape");
+    static_assert(NQB >= 1 && NKB >= 1, "tile shape");
 
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    // Every LDS buffer is its own object: the compiler then knows that the
+    // direct-to-LDS prefetch into one buffer never aliases reads or writes of
+    // another and does not make them wait for it.
+    __shared__ __attribute__((aligned(1024))) char qtile0[QT_BYTES], qtile1[QT_BYTES];   // Q, 64 rows
+    __shared__ __attribute__((aligned(1024))) char otile0[QT_BYTES], otile1[QT_BYTES];   // dO, 64 rows
+    __shared__ __attribute__((aligned(1024))) char ktile[KT_BYTES];                      // K, 128 rows
+    // Per-row statistics of the tile (64 LSE*log2e, then 64 -D), per buffer.
+    __shared__ __attribute__((aligned(16))) float stat0[2 * BQ], stat1[2 * BQ];
+    // P^T then dS^T ([128 keys][64 queries] bf16 each).
+    __shared__ __attribute__((aligned(1024))) char ptbuf[2 * PT_BYTES];
 
     const int BH = a.B * a.H;
     const int kt = blockIdx.x / BH;     // key tile 0 (most queries) first
@@ -171,7 +178,7 @@ void bwd_bf16_kernel(BwdArgs a) {
         const int c = blk * 64 + lane;
         const int row = c / CPR, pch = c % CPR;
         const int64_t off = int64_t(min(k0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off), (lds_void*)(smem + OFF_K + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off), (lds_void*)(ktile + blk * 1024), 16, 0, 0);
     }
     // B operand of dO V^T: lane (key, half hh), k-step ks holds columns
     // 16ks + 8hh .. +7 of the key's V row (K comes from the LDS tile).
@@ -183,7 +190,8 @@ void bwd_bf16_kernel(BwdArgs a) {
     }
 
     // ---- Q / dO / statistics tile copy (direct to LDS, swizzled rows) -------
-    auto copy_q = [&](int q0, int buf) {
+    auto copy_q = [&](int q0, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
 #pragma unroll
         for (int i = 0; i < NQB; ++i) {
             const int blk = wave * NQB + i;
@@ -191,59 +199,57 @@ void bwd_bf16_kernel(BwdArgs a) {
             const int row = c / CPR, pch = c % CPR;
             const int64_t roff = int64_t(min(q0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
             __builtin_amdgcn_global_load_lds((global_cvoid*)(Qg + roff),
-                                             (lds_void*)(smem + OFF_Q + buf * QT_BYTES + blk * 1024), 16, 0, 0);
+                                             (lds_void*)((buf ? qtile1 : qtile0) + blk * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((global_cvoid*)(Og + roff),
-                                             (lds_void*)(smem + OFF_O + buf * QT_BYTES + blk * 1024), 16, 0, 0);
+                                             (lds_void*)((buf ? otile1 : otile0) + blk * 1024), 16, 0, 0);
         }
-        if (wave < 2) {  // wave 0: LSE*log2e of the 64 queries, wave 1: -D
-            const int qq = min(q0 + lane, a.N - 1);
-            const float* src = (wave ? a.ws_nd : a.ws_lse2) + int64_t(bh) * a.N + qq;
-            __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(smem + OFF_L + buf * 512 + wave * 256),
-                                             4, 0, 0);
-        }
+        float* st = buf ? stat1 : stat0;
+        const int qq = min(q0 + lane, a.N - 1);
+        if (wave == 0)       // LSE*log2e of the 64 queries
+            __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_lse2 + int64_t(bh) * a.N + qq),
+                                             (lds_void*)st, 4, 0, 0);
+        else if (wave == 1)  // -D
+            __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_nd + int64_t(bh) * a.N + qq),
+                                             (lds_void*)(st + BQ), 4, 0, 0);
     };
 
-    // per-lane LDS addressing
+    // ---- per-lane LDS offsets ----------------------------------------------
+    // Everything that varies with the buffer, the k-step or the 16-row block
+    // is a compile-time immediate; what remains is a handful of per-lane
+    // offsets (the XOR swizzles of rows 16c + r do not depend on c).
     const int prow = 32 * qh + perm_row(j);                        // Q / dO row-operand row
     const int krow = 32 * kb + j;                                  // K / P^T / dS^T row of this lane's key
     const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
     const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
     const int tr_half = 8 * (lane & 1);
-    const int ds_piece = 4 * ((lane >> 4) & 1) + (lane & 3);       // + 8 * query half
-
-    // A operand of Q K^T / dO V^T: row perm(j) of this wave's query half
-    auto q_operand = [&](const char* tile, int ks) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(tile + prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow)));
-    };
-    // B operand of Q K^T: lane (key, half hh) reads row krow of the K tile
-    auto k_operand = [&](int ks) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(smem + OFF_K + krow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(krow)));
-    };
-    // Transposed operand: lane (column 32dt + j, half hh) gets rows 16c + 8hh .. +7
-    // of that column (A of the dO^T / Q^T products, B of the dQ product).
-    auto tr_operand = [&](const char* tile, int c, int dt) -> bf16x8 {
-        const int r0 = 16 * c + tr_row, r1 = r0 + 4;
-        const int ch = 4 * dt + tr_lch;
-        const short4_t lo = lds_read_tr(tile + r0 * (2 * D) + tr_half + 16 * (ch ^ swz<D>(r0)));
-        const short4_t hi = lds_read_tr(tile + r1 * (2 * D) + tr_half + 16 * (ch ^ swz<D>(r1)));
-        return cat(lo, hi);
-    };
     // P^T / dS^T: 128-byte rows (64 queries) of 8-byte pieces; the 16-byte
     // chunk is XOR-swizzled by row so that per-key row reads (16 lanes, 16
     // keys) and transposing reads (4 consecutive keys) are conflict-free.
-    auto pt_addr = [&](int off, int row, int piece) -> char* {
-        return smem + off + row * 128 + 8 * (piece ^ (2 * (4 * ((row >> 1) & 1) + ((row >> 2) & 3))));
-    };
-    // B operand of dO^T P / Q^T dS: lane (key, half hh) gets queries 16c + 8hh .. +7
-    auto pt_operand = [&](int off, int c) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(pt_addr(off, krow, 4 * c + 2 * hh));
-    };
-    // A operand of dS K: lane (query 32 dqh + j, half hh) gets keys 16ks + 8hh .. +7
-    auto ds_operand = [&](int dqh, int ks) -> bf16x8 {
-        const int r0 = 16 * ks + tr_row, r1 = r0 + 4;
-        return cat(lds_read_tr(pt_addr(OFF_S, r0, 8 * dqh + ds_piece)),
-                   lds_read_tr(pt_addr(OFF_S, r1, 8 * dqh + ds_piece)));
-    };
+    auto pt_swz = [](int row) { return 2 * (4 * ((row >> 1) & 1) + ((row >> 2) & 3)); };
+    int qo[KS], ko[KS];           // row operands: Q/dO rows prow, K rows krow
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qo[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
+        ko[ks] = krow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(krow));
+    }
+    int tro[DT][2];               // transposed reads, rows tr_row (+4) of column block dt
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = tr_row + 4 * e;
+            tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
+        }
+    int pto[BQ / 16];             // P^T row reads (dS^T: + PT_BYTES)
+#pragma unroll
+    for (int c = 0; c < BQ / 16; ++c) pto[c] = krow * 128 + 8 * ((4 * c + 2 * hh) ^ pt_swz(krow));
+    // P^T row writes (dS^T: + PT_BYTES): 16 bytes = queries 32qh + 16c + 8hh .. +7
+    // (the swizzle is even, so pieces p and p + 1 stay adjacent and in order)
+    int pwo[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pwo[c] = krow * 128 + 8 * ((8 * qh + 4 * c + 2 * hh) ^ pt_swz(krow));
+    auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
+    auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
 
     f32x16 acc[DT];   // dV^T (qh = 0) or dK^T (qh = 1) of this wave's 32 keys
 #pragma unroll
@@ -254,37 +260,36 @@ void bwd_bf16_kernel(BwdArgs a) {
     const float c2 = a.scale_log2;
     const int n_qt = (a.N + BQ - 1) / BQ;
     const int qt0 = CAUSAL ? k0 / BQ : 0;
-    const int dq_qh = wave >> 2;                  // dQ output tile of this wave
-    const int dq_dt = wave % DT;
-    const int dq_ks0 = ((wave & 3) / DT) * DQ_KSTEPS;
-    float* dq_acc = a.ws_dq + int64_t(bh) * a.N * D;
 
-    if (qt0 < n_qt) copy_q(qt0 * BQ, 0);
-    for (int it = qt0; it < n_qt; ++it) {
-        const int buf = (it - qt0) & 1;
+    if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
+    // One query tile; `bufc` carries the LDS buffer as a compile-time constant
+    // (the loop below is unrolled by two) so that the compiler can tell the
+    // prefetch target from the buffer being read and does not wait for it.
+    auto step = [&](int it, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const int qt_base = it * BQ;
         const int q0 = qt_base + 32 * qh;         // first query of this wave
+        // tile `it` is in LDS; every wave is done with the previous P^T / dS^T
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // tile `it` is in LDS; every wave is done with the previous P^T / dS^T
-        if (it + 1 < n_qt) copy_q(qt_base + BQ, buf ^ 1);
-        const char* qs = smem + OFF_Q + buf * QT_BYTES;
-        const char* os = smem + OFF_O + buf * QT_BYTES;
-        const float* ls = reinterpret_cast<const float*>(smem + OFF_L + buf * 512) + 32 * qh;
+        __builtin_amdgcn_s_barrier();
+        const char* qt = buf ? qtile1 : qtile0;
+        const char* ot = buf ? otile1 : otile0;
+        const float* ls = (buf ? stat1 : stat0) + 32 * qh;
 
         // S = Q K^T and dP - D (register g = 4r + t of lane half hh: query
         // q0 + 16(r>>1) + 8hh + 4(r&1) + t, key `key`)
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float4 nd = *reinterpret_cast<const float4*>(ls + 64 + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
+            const float4 nd = *reinterpret_cast<const float4*>(ls + BQ + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
             dp[4 * r + 0] = nd.x; dp[4 * r + 1] = nd.y; dp[4 * r + 2] = nd.z; dp[4 * r + 3] = nd.w;
         }
 #pragma unroll
         for (int g = 0; g < 16; ++g) s[g] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_operand(qs, ks), k_operand(ks), s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_operand(os, ks), vreg[ks], dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(qt, qo[ks]), ld16(ktile, ko[ks]), s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(ot, qo[ks]), vreg[ks], dp, 0, 0, 0);
         }
 
         // P = exp2(S c - LSE log2 e), zero for masked (query, key) pairs
@@ -319,43 +324,36 @@ void bwd_bf16_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint4 p4 = __builtin_bit_cast(uint4, pb[c]);
-            const uint4 d4 = __builtin_bit_cast(uint4, dsb[c]);
-            const int piece = 8 * qh + 4 * c + 2 * hh;   // queries 32qh + 16c + 8hh .. +3, then +4 .. +7
-            *reinterpret_cast<uint2*>(pt_addr(OFF_P, krow, piece)) = make_uint2(p4.x, p4.y);
-            *reinterpret_cast<uint2*>(pt_addr(OFF_P, krow, piece + 1)) = make_uint2(p4.z, p4.w);
-            *reinterpret_cast<uint2*>(pt_addr(OFF_S, krow, piece)) = make_uint2(d4.x, d4.y);
-            *reinterpret_cast<uint2*>(pt_addr(OFF_S, krow, piece + 1)) = make_uint2(d4.z, d4.w);
+            *reinterpret_cast<bf16x8*>(ptbuf + pwo[c]) = pb[c];
+            *reinterpret_cast<bf16x8*>(ptbuf + pwo[c] + PT_BYTES) = dsb[c];
         }
-        __syncthreads();  // P^T and dS^T of the whole tile are in LDS
+        // Prefetch the next tile once this iteration's LDS stores are issued
+        // (LDS stores behind a pending direct-to-LDS load get made to wait).
+        if (it + 1 < n_qt) copy_q(qt_base + BQ, std::integral_constant<int, buf ^ 1>{});
+        // P^T and dS^T of the whole tile are in LDS (LDS stores only: the
+        // prefetch just issued stays in flight across this barrier)
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        __builtin_amdgcn_s_barrier();
 
         // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1), over 64 queries
-        {
-            const char* at = qh ? qs : os;
-            const int bo = qh ? OFF_S : OFF_P;
+        auto tile_product = [&](const char* at, auto bo) {
+            constexpr int BO = decltype(bo)::value;
 #pragma unroll
             for (int c = 0; c < BQ / 16; ++c) {
-                const bf16x8 bop = pt_operand(bo, c);
+                const bf16x8 bop = ld16(ptbuf, pto[c] + BO);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(at, c, dt), bop, acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]), bop, acc[dt], 0, 0, 0);
             }
-        }
+        };
+        if (qh) tile_product(qt, std::integral_constant<int, PT_BYTES>{});
+        else    tile_product(ot, std::integral_constant<int, 0>{});
 
-        // dQ[32 dq_qh .., 32 dq_dt ..] += dS K over this wave's key range
-        f32x16 dq;
-#pragma unroll
-        for (int g = 0; g < 16; ++g) dq[g] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < DQ_KSTEPS; ++ks)
-            dq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ds_operand(dq_qh, dq_ks0 + ks),
-                                                          tr_operand(smem + OFF_K, dq_ks0 + ks, dq_dt), dq, 0, 0, 0);
-        // register g of lane half hh: query 8(g>>2) + 4hh + (g&3) of the half, column 32 dq_dt + j
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            const int q = qt_base + 32 * dq_qh + 8 * (g >> 2) + 4 * hh + (g & 3);
-            if (q < a.N) unsafeAtomicAdd(dq_acc + int64_t(q) * D + 32 * dq_dt + j, dq[g]);
-        }
+    };
+    for (int it = qt0; it < n_qt; it += 2) {
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: dV (qh = 0) or dK = scale * (dK^T)^T (qh = 1), bf16 -------
@@ -376,56 +374,186 @@ void bwd_bf16_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. convert: one thread per 8 columns of a row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_convert_kernel(BwdArgs a) {
-    constexpr int LPR = D / 8;
-    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t row = t / LPR;
-    const int l = static_cast<int>(t % LPR);
-    if (row >= int64_t(a.B) * a.H * a.N) return;
-    const int i = static_cast<int>(row % a.N);
-    const int64_t bh = row / a.N;
-    const int b = static_cast<int>(bh / a.H), h = static_cast<int>(bh % a.H);
-    const float4* src = reinterpret_cast<const float4*>(a.ws_dq + row * D + 8 * l);
-    const float4 x0 = src[0], x1 = src[1];
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    bf16x8 y;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = static_cast<__bf16>(xs[e] * a.scale);
-    u16* dst = static_cast<u16*>(a.dq) + int64_t(b) * a.sb + int64_t(h) * a.sh + int64_t(i) * a.ss + 8 * l;
-    *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, y);
-}
-
-template <int D>
-constexpr int main_lds_bytes() { return BK * D * 2 + 4 * BQ * D * 2 + 2 * 512 + 2 * BK * BQ * 2; }
-
+// 3. dQ kernel: 8 waves of 32 queries, 64-key K/V tiles double-buffered.
 template <int D, bool CAUSAL>
-int launch_main(const BwdArgs& a, hipStream_t stream) {
-    constexpr int LDS = main_lds_bytes<D>();
-    auto kern = bwd_bf16_kernel<D, CAUSAL>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr_set = true;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BwdArgs a) {
+    constexpr int NW = 8, BR = 32 * NW, BC = 64;
+    constexpr int KS = D / 16, DT = D / 32, CPR = D / 8;
+    constexpr int TB = BC * D * 2;              // one K or V tile
+    constexpr int NI = TB / 1024 / NW;          // 1 KB copy blocks per wave per tile
+    static_assert(NI >= 1, "tile shape");
+    __shared__ __attribute__((aligned(1024))) char ktile0[TB], ktile1[TB], vtile0[TB], vtile1[TB];
+
+    // ---- work decomposition: heaviest query tiles first, one head per XCD ----
+    const int n_qt = (a.N + BR - 1) / BR;
+    const int total = n_qt * a.B * a.H;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        id = (id & 7) * per + (id >> 3);
     }
-    const int64_t grid = int64_t((a.N + BK - 1) / BK) * a.B * a.H;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), LDS, stream, a);
-    return static_cast<int>(hipGetLastError());
+    const int bh = id / n_qt;
+    int qt = id % n_qt;
+    if (CAUSAL) qt = n_qt - 1 - qt;
+    const int b = bh / a.H, h = bh % a.H;
+    const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
+    const u16* Qg = static_cast<const u16*>(a.q) + base;
+    const u16* Kg = static_cast<const u16*>(a.k) + base;
+    const u16* Vg = static_cast<const u16*>(a.v) + base;
+    const u16* Og = static_cast<const u16*>(a.dout) + base;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int q0 = qt * BR + 32 * wave;         // first query of this wave
+    const int qi = q0 + j;                      // this lane's query
+    const int n_kt = (a.N + BC - 1) / BC;
+    const int nt = CAUSAL ? min(n_kt, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt;
+    int wnt = CAUSAL ? min(nt, (min(a.N, q0 + 32) + BC - 1) / BC) : nt;
+    if (q0 >= a.N) wnt = 0;
+
+    // ---- K/V tile copy (direct to LDS, swizzled rows; rows past the end
+    // re-read the last row, their scores are masked) ---------------------------
+    auto copy_kv = [&](int kt, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int blk = wave * NI + i;
+            const int c = blk * 64 + lane;
+            const int row = c / CPR, pch = c % CPR;
+            const int64_t off = int64_t(min(kt * BC + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
+            __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off),
+                                             (lds_void*)((buf ? ktile1 : ktile0) + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((global_cvoid*)(Vg + off),
+                                             (lds_void*)((buf ? vtile1 : vtile0) + blk * 1024), 16, 0, 0);
+        }
+    };
+
+    // ---- per-query operands and statistics (zero past the end) --------------
+    bf16x8 qreg[KS], oreg[KS];   // B operands of K Q^T / V dO^T: lane (query, half hh)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 xq = make_uint4(0, 0, 0, 0), xo = make_uint4(0, 0, 0, 0);
+        if (qi < a.N) {
+            const int64_t off = int64_t(qi) * a.ss + 16 * ks + 8 * hh;
+            xq = *reinterpret_cast<const uint4*>(Qg + off);
+            xo = *reinterpret_cast<const uint4*>(Og + off);
+        }
+        qreg[ks] = __builtin_bit_cast(bf16x8, xq);
+        oreg[ks] = __builtin_bit_cast(bf16x8, xo);
+    }
+    const float lse2 = qi < a.N ? a.ws_lse2[int64_t(bh) * a.N + qi] : 0.f;
+    const float nd = qi < a.N ? a.ws_nd[int64_t(bh) * a.N + qi] : 0.f;
+
+    // ---- per-lane LDS offsets ----------------------------------------------
+    const int prow = perm_row(j);                                  // K / V row operand (+32 st)
+    const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
+    const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
+    const int tr_half = 8 * (lane & 1);
+    int ro[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ro[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
+    int tro[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = tr_row + 4 * e;
+            tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
+        }
+    auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
+    auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
+
+    f32x16 acc[DT];   // dQ^T: register g of lane half hh holds column 32dt + 8(g>>2) + 4hh + (g&3)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
+    const float c2 = a.scale_log2;
+
+    // One key tile: per 32-key subtile st, S^T and dP^T - D, then P^T and
+    // dS^T; register g = 4r + t of lane half hh holds key
+    // 32st + 16(r>>1) + 8hh + 4(r&1) + t, so the bf16 dS^T registers are the B
+    // operand of the 16-key chunk c = 2st + (r>>1).
+    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds) {
+        const bool edge = (kt * BC + BC > a.N) || (CAUSAL && kt * BC + BC - 1 > q0);
+        const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - kt * BC - 8 * hh;
+        bf16x8 dsb[2][2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            f32x16 s, dp;
+#pragma unroll
+            for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(kt_lds, 32 * st * 2 * D + ro[ks]), qreg[ks], s,
+                                                             0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(vt_lds, 32 * st * 2 * D + ro[ks]), oreg[ks], dp,
+                                                              0, 0, 0);
+            }
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                float x = fmaf(s[g], c2, -lse2);
+                if (edge) {
+                    const int r = g >> 2, t = g & 3;
+                    if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) x = -INFINITY;
+                }
+                dsb[st][g >> 3][g & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x) * dp[g]);
+            }
+        }
+        // dQ^T += K^T dS^T over the tile's four 16-key chunks
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    ldtr(kt_lds, 16 * c * 2 * D + tro[dt][0], 16 * c * 2 * D + tro[dt][1]), dsb[c >> 1][c & 1],
+                    acc[dt], 0, 0, 0);
+    };
+
+    if (nt > 0) copy_kv(0, std::integral_constant<int, 0>{});
+    auto step = [&](int kt, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();   // tile kt is in LDS; everyone is done with tile kt - 1
+        if (kt + 1 < nt) copy_kv(kt + 1, std::integral_constant<int, buf ^ 1>{});
+        if (kt < wnt) compute(kt, buf ? ktile1 : ktile0, buf ? vtile1 : vtile0);
+    };
+    for (int kt = 0; kt < nt; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nt) step(kt + 1, std::integral_constant<int, 1>{});
+    }
+
+    // ---- epilogue: dQ = scale * (dQ^T)^T, bf16 -------------------------------
+    if (qi < a.N) {
+        u16* row = static_cast<u16*>(a.dq) + base + int64_t(qi) * a.ss;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                __bf16 x4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * a.scale);
+                *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
+            }
+    }
 }
 
 template <int D>
 int run(const BwdArgs& a, hipStream_t s) {
     const int64_t threads = int64_t(a.B) * a.H * a.N * (D / 8);
-    const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
-    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
     int err = static_cast<int>(hipGetLastError());
     if (err) return err;
-    err = a.causal ? launch_main<D, true>(a, s) : launch_main<D, false>(a, s);
-    if (err) return err;
-    hipLaunchKernelGGL(bwd_convert_kernel<D>, dim3(blocks), dim3(256), 0, s, a);
+    const unsigned g_kv = static_cast<unsigned>(int64_t((a.N + BK - 1) / BK) * a.B * a.H);
+    if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(512), 0, s, a);
+    if ((err = static_cast<int>(hipGetLastError()))) return err;
+    const unsigned g_q = static_cast<unsigned>(int64_t((a.N + 255) / 256) * a.B * a.H);
+    if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(g_q), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(g_q), dim3(512), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -51,8 +51,8 @@ struct Fp8Args {
     int32_t tile_cfg;
 };
 
-// Backward arguments (bf16 tensors sharing one layout; fp32 workspace split
-// into the dQ accumulator [B, H, N, D] and two per-row arrays [B, H, N]).
+// Backward arguments (bf16 tensors sharing one layout; fp32 workspace of two
+// per-row arrays [B, H, N]).
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -68,15 +68,14 @@ struct BwdArgs {
     float scale;
     float scale_log2;
     int32_t causal;
-    float* ws_dq;         // [B, H, N, D] fp32 accumulator
     float* ws_lse2;       // [B, H, N] LSE * log2(e)
     float* ws_nd;         // [B, H, N] -rowsum(dO o O)
 };
 
 // Workspace bytes of the backward pass (each part 256-byte aligned).
 inline int64_t bwd_ws_part(int64_t n) { return (n * 4 + 255) / 256 * 256; }
-inline int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
-    return bwd_ws_part(B * H * N * D) + 2 * bwd_ws_part(B * H * N);
+inline int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+    return 2 * bwd_ws_part(B * H * N);
 }
 
 // Launchers: return a hipError_t value (0 = success).

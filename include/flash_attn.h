@@ -175,12 +175,12 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
  *   dq, dk, dv       : [layout] bf16 outputs (rounded to nearest even)
  *   causal, scale    : as given to the forward
  *   workspace        : device memory of at least
- *                      flash_attn_bwd_workspace_size(layout, dtype) bytes,
- *                      256-byte aligned, owned by the caller; its contents on
- *                      entry do not matter and are overwritten (dQ is
- *                      accumulated there in fp32 with atomic adds, so the
- *                      summation order of dQ, and its last bits, can vary
- *                      from call to call; dK and dV are deterministic).
+ *                      flash_attn_bwd_workspace_size(layout, dtype) bytes
+ *                      (two fp32 values per query row), 256-byte aligned,
+ *                      owned by the caller; its contents on entry do not
+ *                      matter and are overwritten.
+ * The result is deterministic: dK/dV are summed over query tiles and dQ over
+ * key tiles inside one workgroup each, in a fixed order (no atomics).
  * Errors: as flash_attn_fwd; dtype F32 -> ERR_UNSUPPORTED (bf16 only);
  * workspace NULL, too small or misaligned -> ERR_WORKSPACE.
  */
