@@ -50,17 +50,16 @@ def parse():
 
 
 def measured_traffic(w):
-    """HBM bytes per launch recorded under profiles/ for this workload's kernel,
-    or None when the kernel source has changed since the counters were taken."""
-    import hashlib
+    """HBM bytes per call recorded under profiles/ for this workload, or None
+    when the kernel source or its build flags changed since the counters were
+    taken (the record keeps the fingerprint of every source it covers)."""
+    from exact_attention_77_amd.build import fingerprint
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))[w.name]
-    except (OSError, KeyError, ValueError):
-        return None
-    src = os.path.join(ROOT, rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if sha != rec["source_sha256_16"]:
+        if any(fingerprint(src) != fp for src, fp in rec["fingerprints"].items()):
+            return None
+    except (OSError, KeyError, ValueError, AttributeError):
         return None
     return rec["read_bytes"] + rec["write_bytes"]
 

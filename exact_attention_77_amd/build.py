@@ -35,6 +35,15 @@ PER_FILE = {
 }
 
 
+def fingerprint(src: str) -> str:
+    """sha256 prefix of a csrc/ source file plus the flags it is compiled with:
+    it changes whenever the kernel binary built from that file can change."""
+    import hashlib
+    h = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read())
+    h.update(repr((COMMON, PER_FILE.get(src, []), ARCH)).encode())
+    return h.hexdigest()[:16]
+
+
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
