@@ -286,10 +286,24 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int g = 0; g < 16; ++g) s[g] = 0.f;
+        {   // 2*KS products alternating S / dP - D; LDS operands read two ahead
+            auto srcA = [&](int m) { return ld16((m & 1) ? ot : qt, qo[m >> 1]); };
+            bf16x8 opA[3], opK[3];
+            opA[0] = srcA(0); opK[0] = ld16(ktile, ko[0]);
+            opA[1] = srcA(1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(qt, qo[ks]), ld16(ktile, ko[ks]), s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(ot, qo[ks]), vreg[ks], dp, 0, 0, 0);
+            for (int m = 0; m < 2 * KS; ++m) {
+                if (m + 2 < 2 * KS) {
+                    opA[(m + 2) % 3] = srcA(m + 2);
+                    if (!(m & 1)) opK[(m + 2) % 3] = ld16(ktile, ko[(m + 2) >> 1]);
+                }
+                if (m & 1)
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], vreg[m >> 1], dp, 0, 0, 0);
+                else
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], opK[m % 3], s, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         // P = exp2(S c - LSE log2 e), zero for masked (query, key) pairs
@@ -338,13 +352,23 @@ void bwd_dkdv_kernel(BwdArgs a) {
         // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1), over 64 queries
         auto tile_product = [&](const char* at, auto bo) {
             constexpr int BO = decltype(bo)::value;
+            constexpr int NP = BQ / 16 * DT;   // products; A operands read two ahead
+            auto src = [&](int n) {
+                const int c = n / DT, dt = n % DT;
+                return ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
+            };
+            bf16x8 op[3], bop = ld16(ptbuf, pto[0] + BO);
+            op[0] = src(0);
+            op[1] = src(1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int c = 0; c < BQ / 16; ++c) {
-                const bf16x8 bop = ld16(ptbuf, pto[c] + BO);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]), bop, acc[dt], 0, 0, 0);
+            for (int n = 0; n < NP; ++n) {
+                if (n + 2 < NP) op[(n + 2) % 3] = src(n + 2);
+                const int c = n / DT, dt = n % DT;
+                const bf16x8 b = bop;
+                if (dt == DT - 1 && c + 1 < BQ / 16) bop = ld16(ptbuf, pto[c + 1] + BO);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], b, acc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         if (qh) tile_product(qt, std::integral_constant<int, PT_BYTES>{});
@@ -374,11 +398,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ kernel: 8 waves of 32 queries, 64-key K/V tiles double-buffered.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+// 3. dQ kernel: NW waves of 32 queries, BC-key K/V tiles double-buffered
+// (processed in 64-key blocks).
+template <int D, bool CAUSAL, int NW, int BC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(BwdArgs a) {
-    constexpr int NW = 8, BR = 32 * NW, BC = 64;
+    constexpr int BR = 32 * NW;
+    static_assert(BC % 64 == 0, "key tile");
     constexpr int KS = D / 16, DT = D / 32, CPR = D / 8;
     constexpr int TB = BC * D * 2;              // one K or V tile
     constexpr int NI = TB / 1024 / NW;          // 1 KB copy blocks per wave per tile
@@ -473,44 +499,69 @@ void bwd_dq_kernel(BwdArgs a) {
         for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
     const float c2 = a.scale_log2;
 
-    // One key tile: per 32-key subtile st, S^T and dP^T - D, then P^T and
-    // dS^T; register g = 4r + t of lane half hh holds key
-    // 32st + 16(r>>1) + 8hh + 4(r&1) + t, so the bf16 dS^T registers are the B
-    // operand of the 16-key chunk c = 2st + (r>>1).
-    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds) {
-        const bool edge = (kt * BC + BC > a.N) || (CAUSAL && kt * BC + BC - 1 > q0);
-        const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - kt * BC - 8 * hh;
-        bf16x8 dsb[2][2];
+    // One key tile, in 64-key blocks: per 32-key subtile st, S^T and dP^T - D,
+    // then P^T and dS^T; register g = 4r + t of lane half hh holds key
+    // 32st + 16(r>>1) + 8hh + 4(r&1) + t of the block, so the bf16 dS^T
+    // registers are the B operand of the block's 16-key chunk c = 2st + (r>>1).
+    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            f32x16 s, dp;
+        for (int kb = 0; kb < BC / 64; ++kb) {
+            const int k_lo = kt * BC + 64 * kb;
+            if (CAUSAL && kb > 0 && k_lo > q0 + 31) continue;   // wave-uniform: block fully masked
+            const bool edge = (k_lo + 64 > a.N) || (CAUSAL && k_lo + 63 > q0);
+            const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 8 * hh;
+            const char* kb_lds = kt_lds + 64 * kb * 2 * D;
+            const char* vb_lds = vt_lds + 64 * kb * 2 * D;
+            bf16x8 dsb[2][2];
 #pragma unroll
-            for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
+            for (int st = 0; st < 2; ++st) {
+                f32x16 s, dp;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(kt_lds, 32 * st * 2 * D + ro[ks]), qreg[ks], s,
-                                                             0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16(vt_lds, 32 * st * 2 * D + ro[ks]), oreg[ks], dp,
-                                                              0, 0, 0);
-            }
+                for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
+                // 2*KS products alternating S^T / dP^T; LDS operands read two ahead
+                auto src = [&](int m) {
+                    return ld16((m & 1) ? vb_lds : kb_lds, 32 * st * 2 * D + ro[m >> 1]);
+                };
+                bf16x8 op[3];
+                op[0] = src(0);
+                op[1] = src(1);
 #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                float x = fmaf(s[g], c2, -lse2);
-                if (edge) {
-                    const int r = g >> 2, t = g & 3;
-                    if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) x = -INFINITY;
+                for (int m = 0; m < 2 * KS; ++m) {
+                    if (m + 2 < 2 * KS) op[(m + 2) % 3] = src(m + 2);
+                    if (m & 1)
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], oreg[m >> 1], dp, 0, 0, 0);
+                    else
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], qreg[m >> 1], s, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                dsb[st][g >> 3][g & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x) * dp[g]);
+#pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    float x = fmaf(s[g], c2, -lse2);
+                    if (edge) {
+                        const int r = g >> 2, t = g & 3;
+                        if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) x = -INFINITY;
+                    }
+                    dsb[st][g >> 3][g & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x) * dp[g]);
+                }
+            }
+            // dQ^T += K^T dS^T over the block's four 16-key chunks (operands two ahead)
+            constexpr int NQ = 4 * DT;
+            auto tsrc = [&](int n) {
+                const int c = n / DT, dt = n % DT;
+                return ldtr(kb_lds, 16 * c * 2 * D + tro[dt][0], 16 * c * 2 * D + tro[dt][1]);
+            };
+            bf16x8 top[3];
+            top[0] = tsrc(0);
+            top[1] = tsrc(1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+                if (n + 2 < NQ) top[(n + 2) % 3] = tsrc(n + 2);
+                const int c = n / DT, dt = n % DT;
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[n % 3], dsb[c >> 1][c & 1], acc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // dQ^T += K^T dS^T over the tile's four 16-key chunks
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    ldtr(kt_lds, 16 * c * 2 * D + tro[dt][0], 16 * c * 2 * D + tro[dt][1]), dsb[c >> 1][c & 1],
-                    acc[dt], 0, 0, 0);
     };
 
     if (nt > 0) copy_kv(0, std::integral_constant<int, 0>{});
@@ -551,9 +602,10 @@ int run(const BwdArgs& a, hipStream_t s) {
     if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(512), 0, s, a);
     if ((err = static_cast<int>(hipGetLastError()))) return err;
-    const unsigned g_q = static_cast<unsigned>(int64_t((a.N + 255) / 256) * a.B * a.H);
-    if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(g_q), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(g_q), dim3(512), 0, s, a);
+    constexpr int NW = 8, BC = 128;   // dQ kernel: 256 queries per workgroup, 128-key tiles
+    const unsigned g_q = static_cast<unsigned>(int64_t((a.N + 32 * NW - 1) / (32 * NW)) * a.B * a.H);
+    if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
