@@ -7,7 +7,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 The numerics live in ``oracle.c`` (plain two-pass fp64 attention, its analytic
 gradient, an OCP e4m3 codec, a dense Hadamard rotation and block quantisation);
 this module compiles it with gcc on first use and wraps it with ctypes over
-numpy arrays.  See ``oracle.c`` for the passages each function follows:
+numpy arrays.  The (O, LSE) merge of partial results is plain numpy here.  See ``oracle.c`` for the passages each function follows:
 "FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析" sec. 2.1, 6.1,
 7.2, 11.3 and "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
 Low-precision" sec. 技術 3 / 数値誤差.
@@ -222,3 +222,27 @@ def fp8_per_tensor_baseline(q, k, v, causal: bool = False, scale: float | None =
         c, sc = quantize_per_tensor(x)
         deq.append(e4m3_decode(c) * sc)
     return attn_fwd(deq[0], deq[1], deq[2], causal=causal, scale=scale, rows=rows, p_quant=True)
+
+
+def merge(o_parts, lse_parts):
+    """Attention over the union of disjoint key sets from the results over each
+    set, fp64 ("FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析"
+    sec. 6.2-6.3: the running sum and output are rescaled to a common maximum
+    and added; here every part is already normalised, so its sum is exp(LSE_s)).
+
+    o_parts: [S, ..., d] normalised outputs; lse_parts: [S, ...] natural-log LSE.
+    Returns (o, lse) with LSE = ln sum_s exp(LSE_s) and
+    o = sum_s exp(LSE_s - LSE) o_s.  A row whose parts all have LSE = -inf
+    (no key at all) gets o = 0 and LSE = -inf.
+    """
+    o = _f64(o_parts)
+    lse = _f64(lse_parts)
+    assert o.shape[:-1] == lse.shape and lse.shape[0] >= 1
+    m = lse.max(axis=0)                      # common reference: the largest LSE
+    alive = np.isfinite(m)
+    m0 = np.where(alive, m, 0.0)
+    w = np.exp(lse - m0)                     # exp(-inf) = 0 for empty parts
+    total = w.sum(axis=0)
+    lse_out = np.where(alive, m0 + np.log(np.where(alive, total, 1.0)), -np.inf)
+    frac = np.where(alive, w / np.where(alive, total, 1.0), 0.0)
+    return (frac[..., None] * o).sum(axis=0), lse_out
