@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=8192, d=128) and % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}   # MI355X dense, published
+PEAK_HBM_GBS = 8000.0                                             # MI355X HBM3E, published
 
 
 def parse():
@@ -118,6 +119,8 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if w.parts:
+        return bench_merge(args, w, dev)
     if w.backward:
         q, k, v, dout = normal_qkv(w.B, w.H, w.N, w.d, w.seed, with_dout=True)
         dout = to_bf16(dout)[0].to(dev)
@@ -232,6 +235,69 @@ def main():
         out["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_merge(args, w, dev):
+    """The (O, LSE) merge: an HBM stream, reported in GB/s of algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    import exact_attention_77_amd as fa
+    from synth_inputs import merge_parts
+
+    o_parts, lse_parts = merge_parts(w, dev)
+    o = torch.empty(o_parts.shape[1:], dtype=o_parts.dtype, device=dev)
+    lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.flash_attn_merge(o_parts, lse_parts, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_ev = ev0.elapsed_time(ev1) / args.steps
+    ms = max(ms_ev, (time.perf_counter() - t0) * 1e3 / args.steps)
+    gbs = w.merge_bytes / (ms * 1e-3) / 1e9
+    kgbs = w.merge_bytes / (ms_ev * 1e-3) / 1e9
+    out = {
+        "metric": f"attention merge GB/s ({w.name})", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded device draws: O ~ N(0,1) bf16, LSE ~ 7 + 2 N(0,1))",
+        "config": {"workload": w.name, "parts": w.parts, "batch": w.B, "heads": w.H, "seq_len": w.N,
+                   "head_dim": w.d, "bytes_per_step": w.merge_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w),
+                     "kernel_ms": round(ms_ev, 5)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        S, B, H, N, d = o_parts.shape
+        order = np.random.Generator(np.random.PCG64(12345)).permutation(B * H)
+        done, t_total = 0, 0.0
+        for bh in order:
+            b, h = divmod(int(bh), H)
+            op = o_parts[:, b, h].float().cpu().numpy()
+            lp = lse_parts[:, b, h].cpu().numpy()
+            t1 = time.perf_counter()
+            oracle.merge(op, lp)
+            t_total += time.perf_counter() - t1
+            done += 1
+            if t_total >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {"value": round(done * w.merge_bytes / (B * H) / t_total / 1e9, 3),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "seconds": round(t_total, 3),
+                               "sample": f"{done} of {B * H} (batch, head) slices, every row, fp64 numpy"}
     print(json.dumps(out), flush=True)
 
 

@@ -8,6 +8,7 @@ for device memory and the current stream.  The functions carry the C names:
     flash_attn_fp8_quantize(x, role, rotate=False, signs=None) -> (x_fp8, scales)
     flash_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale) -> (o_bf16, lse)
     flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+    flash_attn_merge(o_parts, lse_parts) -> (o, lse)
 
 If the shared library is missing this module raises on first use: there is no
 fallback path.
@@ -22,7 +23,7 @@ import threading
 __all__ = [
     "FlashAttnError", "lib_path", "load", "flash_attn_fwd", "flash_attn_fp8_quantize",
     "flash_attn_fwd_fp8", "flash_attn_fp8_buffer_bytes", "flash_attn_fp8_num_scales",
-    "flash_attn_bwd", "flash_attn_bwd_workspace_size",
+    "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_merge",
     "flash_attn_status_str", "flash_attn_last_error", "flash_attn_abi_version", "Layout",
     "FwdOpts", "STATUS", "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "ROLE_Q", "ROLE_K",
     "ROLE_V", "EXPORTED_SYMBOLS",
@@ -44,8 +45,8 @@ STATUS = {
 EXPORTED_SYMBOLS = (
     "flash_attn_fwd", "flash_attn_fp8_quantize", "flash_attn_fp8_buffer_bytes",
     "flash_attn_fp8_num_scales", "flash_attn_fwd_fp8", "flash_attn_bwd",
-    "flash_attn_bwd_workspace_size", "flash_attn_status_str", "flash_attn_last_error",
-    "flash_attn_abi_version",
+    "flash_attn_bwd_workspace_size", "flash_attn_merge", "flash_attn_status_str",
+    "flash_attn_last_error", "flash_attn_abi_version",
 )
 
 
@@ -98,6 +99,8 @@ def load():
         lib.flash_attn_bwd.restype = I
         lib.flash_attn_bwd_workspace_size.argtypes = [Layout, I]
         lib.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.flash_attn_merge.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P, Layout, I, P]
+        lib.flash_attn_merge.restype = I
         lib.flash_attn_status_str.argtypes = [I]
         lib.flash_attn_status_str.restype = ctypes.c_char_p
         lib.flash_attn_last_error.argtypes = []
@@ -283,3 +286,29 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | N
                                  int(bool(causal)), float(scale), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream()))
     return tuple(outs)
+
+
+def flash_attn_merge(o_parts, lse_parts, out=None, lse=None):
+    """Merge results over disjoint key sets: o_parts [S, B, H, N, d] (float32
+    or bfloat16, each part with the same strides, head_dim contiguous),
+    lse_parts float32 [S, B, H, N] contiguous -> (o [B, H, N, d], lse [B, H, N])."""
+    import torch
+    if o_parts.dtype not in (torch.float32, torch.bfloat16):
+        raise FlashAttnError(4, f"unsupported dtype {o_parts.dtype}")
+    if o_parts.dim() != 5 or lse_parts.shape != o_parts.shape[:4]:
+        raise FlashAttnError(2, "o_parts [S, B, H, N, d] and lse_parts [S, B, H, N]")
+    if lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise FlashAttnError(3, "lse_parts must be contiguous float32")
+    S, B, H, N, d = o_parts.shape
+    lay = _layout_of(o_parts[0])
+    if out is None:
+        out = torch.empty_strided((B, H, N, d), o_parts.stride()[1:], dtype=o_parts.dtype,
+                                  device=o_parts.device)
+    elif out.stride() != o_parts.stride()[1:] or out.dtype != o_parts.dtype:
+        raise FlashAttnError(3, "out must have a part's strides and dtype")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    dt = DTYPE_BF16 if o_parts.dtype == torch.bfloat16 else DTYPE_F32
+    _check(load().flash_attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, o_parts.stride(0),
+                                   out.data_ptr(), lse.data_ptr(), lay, dt, _stream()))
+    return out, lse

@@ -21,6 +21,7 @@ flash_attn_status hip_status(int err) {
 }
 
 constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxMergeParts = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -243,6 +244,34 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
     a.ws_lse2 = reinterpret_cast<float*>(ws);
     a.ws_nd = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows));
     return hip_status(fa::launch_bwd_bf16(a, stream));
+}
+
+flash_attn_status flash_attn_merge(const void* o_parts, const float* lse_parts, int64_t n_parts,
+                                   int64_t part_stride, void* o, float* lse,
+                                   flash_attn_layout layout, flash_attn_dtype dtype, void* stream) {
+    flash_attn_status st = check_shape(layout);
+    if (st != FLASH_ATTN_OK) return st;
+    if (dtype != FLASH_ATTN_F32 && dtype != FLASH_ATTN_BF16) return FLASH_ATTN_ERR_DTYPE;
+    if (n_parts < 1 || n_parts > kMaxMergeParts) return FLASH_ATTN_ERR_ARG;
+    if (is_empty(layout)) return FLASH_ATTN_OK;
+    if (!o_parts || !lse_parts || !o || !lse) return FLASH_ATTN_ERR_NULL;
+    const int64_t eb = (dtype == FLASH_ATTN_F32) ? 4 : 2;
+    if ((st = check_strides(layout, eb)) != FLASH_ATTN_OK) return st;
+    if (n_parts > 1 && (part_stride <= 0 || part_stride % (16 / eb))) return FLASH_ATTN_ERR_LAYOUT;
+    if (!aligned16(o_parts) || !aligned16(o) || (reinterpret_cast<uintptr_t>(lse_parts) & 3u) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return FLASH_ATTN_ERR_LAYOUT;
+    fa::MergeArgs a;
+    a.o_parts = o_parts; a.lse_parts = lse_parts; a.o = o; a.lse = lse;
+    a.sb = layout.stride_b; a.sh = layout.stride_h; a.ss = layout.stride_s;
+    a.part_stride = part_stride;
+    a.B = static_cast<int32_t>(layout.batch);
+    a.H = static_cast<int32_t>(layout.heads);
+    a.N = static_cast<int32_t>(layout.seqlen);
+    a.D = static_cast<int32_t>(layout.head_dim);
+    a.S = static_cast<int32_t>(n_parts);
+    a.bf16 = (dtype == FLASH_ATTN_BF16);
+    return hip_status(fa::launch_merge(a, stream));
 }
 
 const char* flash_attn_status_str(flash_attn_status s) {

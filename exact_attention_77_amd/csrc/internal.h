@@ -72,6 +72,17 @@ struct BwdArgs {
     float* ws_nd;         // [B, H, N] -rowsum(dO o O)
 };
 
+// Merge of attention results over disjoint key sets.
+struct MergeArgs {
+    const void* o_parts;   // part s at o_parts + s * part_stride, strides below
+    const float* lse_parts;  // contiguous [S, B, H, N]
+    void* o;               // same strides as a part
+    float* lse;            // contiguous [B, H, N]
+    int64_t sb, sh, ss, part_stride;
+    int32_t B, H, N, D, S;
+    int32_t bf16;
+};
+
 // Workspace bytes of the backward pass (each part 256-byte aligned).
 inline int64_t bwd_ws_part(int64_t n) { return (n * 4 + 255) / 256 * 256; }
 inline int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
@@ -84,6 +95,7 @@ int launch_fwd_f32(const FwdArgs& a, void* stream);
 int launch_fp8_quantize(const QuantArgs& a, void* stream);
 int launch_fwd_fp8(const Fp8Args& a, void* stream);
 int launch_bwd_bf16(const BwdArgs& a, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
 
 // Rows per scale block the fp8 attention kernel is built for (Q: a wave's
 // 32 query rows; K: the 32 keys one lane half holds; V: one 64-key tile), and

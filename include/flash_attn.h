@@ -195,6 +195,32 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
  * empty shape, an invalid one or a dtype the backward does not accept). */
 size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype dtype);
 
+/*
+ * Merge of attention results over disjoint key sets (the combine step of
+ * attention sharded along the sequence).  Part s holds, for every row, the
+ * normalised output O_s over its keys and the natural-log LSE_s of its scaled
+ * scores, as flash_attn_fwd returns them.  The result over the union of the
+ * keys is
+ *     LSE = ln sum_s exp(LSE_s),    O = sum_s exp(LSE_s - LSE) O_s,
+ * the rescale-and-add update of the online softmax
+ * ("FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析" sec. 6.2,
+ * exact by the rescaling identity of sec. 6.3) applied to whole parts.  A
+ * part with LSE_s = -inf (no key) contributes nothing; a row with no key in
+ * any part gets O = 0 and LSE = -inf.
+ *   o_parts     : n_parts tensors of `dtype` (F32 or BF16), part s at
+ *                 o_parts + s * part_stride elements, each with `layout`
+ *   lse_parts   : fp32 contiguous [n_parts, batch, heads, seqlen]
+ *   n_parts     : 1 .. 4096
+ *   part_stride : elements between parts (> 0 and a multiple of 16 bytes'
+ *                 worth when n_parts > 1)
+ *   o, lse      : outputs, o with `layout` and `dtype`, lse fp32 [B, H, N]
+ * Errors: as flash_attn_fwd; n_parts out of range -> ERR_ARG; bad
+ * part_stride -> ERR_LAYOUT.
+ */
+flash_attn_status flash_attn_merge(const void* o_parts, const float* lse_parts, int64_t n_parts,
+                                   int64_t part_stride, void* o, float* lse,
+                                   flash_attn_layout layout, flash_attn_dtype dtype, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* flash_attn_status_str(flash_attn_status s);
 

@@ -13,7 +13,10 @@ Recipe (the pages benchmark on random synthetic tensors, no dataset):
     ``u < 1e-3`` are multiplied by 20;
   * bf16 tensors are the float32 draws rounded to nearest-even by torch's cast;
     the oracle receives the exact fp64 upcast of the bf16 values;
-  * the +-1 signs of the Hadamard rotation come from their own stream (seed 103).
+  * the +-1 signs of the Hadamard rotation come from their own stream (seed 103);
+  * merge workloads: partial outputs and LSEs drawn on the device with a seeded
+    torch generator (O ~ N(0, 1) as bf16, LSE ~ 7 + 2 N(0, 1), about the LSE of
+    a 1024-key shard of N(0, 1) scores).
 """
 from __future__ import annotations
 
@@ -34,6 +37,7 @@ class Workload:
     seed: int
     outliers: bool = False
     backward: bool = False
+    parts: int = 0          # > 0: merge of this many partial results
 
     @property
     def scale(self) -> float:
@@ -46,8 +50,15 @@ class Workload:
         f = (10.0 if self.backward else 4.0) * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
+    @property
+    def merge_bytes(self) -> int:
+        """HBM bytes a merge must move: every part's O and LSE read once, O and
+        LSE written once (bf16 O, fp32 LSE)."""
+        rows = self.B * self.H * self.N
+        return (self.parts + 1) * (rows * self.d * 2 + rows * 4)
 
-# The five workloads the benchmark targets and parity cases are built on.
+
+# The workloads the benchmark targets and parity cases are built on.
 WORKLOADS = {
     "tiny_f32": Workload("tiny_f32", 1, 1, 128, 64, "f32", False, 0),
     "bf16_n2048_d64": Workload("bf16_n2048_d64", 4, 16, 2048, 64, "bf16", False, 1),
@@ -55,6 +66,9 @@ WORKLOADS = {
     "fp8_n8192_d128": Workload("fp8_n8192_d128", 2, 16, 8192, 128, "fp8", False, 3, outliers=True),
     "bf16_bwd_causal_n4096_d128": Workload("bf16_bwd_causal_n4096_d128", 2, 16, 4096, 128, "bf16",
                                            True, 4, backward=True),
+    # combine step of the headline shape sharded over 8 key ranges
+    "merge_bf16_s8_n8192_d128": Workload("merge_bf16_s8_n8192_d128", 2, 16, 8192, 128, "bf16", False, 5,
+                                         parts=8),
 }
 
 
@@ -107,3 +121,13 @@ def sample_rows(B, H, N, count, seed):
     fixed = [0, min(1, N - 1), N - 1, (B * H - 1) * N, (B * H - 1) * N + N - 1]
     rnd = g.integers(0, total, size=max(count - len(fixed), 0))
     return np.unique(np.concatenate([np.asarray(fixed, np.int64), rnd.astype(np.int64)]))
+
+
+def merge_parts(w, device):
+    """Seeded device tensors (o_parts bf16 [S, B, H, N, d], lse_parts fp32
+    [S, B, H, N]) for a merge workload."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    o = torch.randn((w.parts, w.B, w.H, w.N, w.d), generator=gen, device=device).to(torch.bfloat16)
+    lse = 7.0 + 2.0 * torch.randn((w.parts, w.B, w.H, w.N), generator=gen, device=device)
+    return o, lse

@@ -174,3 +174,18 @@ def test_bwd_validation():
     assert bwd(ws=P + 16, ws_bytes=need) == 7
     assert bwd(lay=_lay(N=0), ws=None, ws_bytes=0, **{n: None for n in ("q", "k", "v", "o", "lse",
                                                                       "dout", "dq", "dk", "dv")}) == 0
+
+
+def merge(o_parts=P, lse_parts=P, n=2, part_stride=1 << 20, o=P, lse=P, lay=None, dtype=fa.DTYPE_BF16):
+    return fa.load().flash_attn_merge(o_parts, lse_parts, n, part_stride, o, lse, lay or _lay(),
+                                      dtype, None)
+
+
+def test_merge_validation():
+    assert merge(o_parts=None) == 1 and merge(lse=None) == 1
+    assert merge(n=0) == 6 and merge(n=4097) == 6
+    assert merge(part_stride=0) == 3 and merge(part_stride=12) == 3
+    assert merge(dtype=fa.DTYPE_FP8_E4M3) == 4
+    assert merge(lay=_lay(d=96)) == 5
+    assert merge(o=P + 8) == 3
+    assert merge(o_parts=None, lse_parts=None, o=None, lse=None, lay=_lay(N=0)) == 0
