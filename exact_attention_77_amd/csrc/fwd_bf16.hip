@@ -39,8 +39,9 @@
 //    each), one workgroup barrier per tile.
 //  * workgroups are renumbered so that the tiles of one head run on one XCD
 //    (the hardware deals workgroup ids round-robin over the 8 XCDs), which
-//    keeps that head's K/V in the XCD's L2; under the causal mask the heaviest
-//    query tiles of a head start first.
+//    keeps that head's K/V in the XCD's L2; under the causal mask a workgroup
+//    processes a heavy and a light query tile of one head (tiles T-1-p and
+//    p), so all workgroups carry equal work.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <math.h>
@@ -102,10 +103,9 @@ __device__ __forceinline__ short4_t lds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((__attribute__((address_space(3))) char*)(p)));
 }
 
-// At most 256 registers per lane so that two waves share each SIMD.
+// One 256-query tile (NW waves of 32 queries) of head bh.
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int bh, int qt) {
     using TL = Tile<D>;
     constexpr int BR = NW * WQ;                       // query rows per workgroup
     constexpr int KSTEPS = D / 16;
@@ -113,19 +113,6 @@ void fwd_bf16_kernel(FwdArgs a) {
     constexpr int NI = TL::BYTES / 1024 / NW;         // 1 KB direct loads per wave per tile
     static_assert(NI >= 1 && TL::BYTES % (1024 * NW) == 0, "tile / wave mismatch");
 
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-
-    // ---- work decomposition -------------------------------------------------
-    const int n_qt = (a.N + BR - 1) / BR;
-    const int total = n_qt * a.B * a.H;
-    int id = blockIdx.x;
-    if ((total & 7) == 0) {  // one contiguous range of (head, tile) per XCD
-        const int per = total >> 3;
-        id = (id & 7) * per + (id >> 3);
-    }
-    const int bh = id / n_qt;
-    int qt = id % n_qt;
-    if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest tile of the head first
     const int b = bh / a.H, h = bh % a.H;
     const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
     const u16* Qg = static_cast<const u16*>(a.q) + base;
@@ -402,6 +389,36 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
+// Work decomposition.  Workgroup ids are renumbered so that each XCD (the
+// hardware deals ids round-robin over the 8 XCDs) owns a contiguous range of
+// heads, whose K/V then stay in that XCD's L2.  Under the causal mask tile qt
+// needs qt + 1 key tiles; a workgroup takes the pair (T-1-p, p) of a head's T
+// query tiles, so every workgroup has the same T + 1 tiles of work (the
+// heavier one first) and the grid is balanced without any dynamic queue.
+// At most 256 registers per lane so that two waves share each SIMD.
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_bf16_kernel(FwdArgs a) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    constexpr int BR = NW * WQ;
+    const int n_qt = (a.N + BR - 1) / BR;
+    const int per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+    const int total = per_head * a.B * a.H;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        id = (id & 7) * per + (id >> 3);
+    }
+    const int bh = id / per_head, p = id % per_head;
+    const int hi = CAUSAL ? n_qt - 1 - p : p;
+    const int n_tiles = (CAUSAL && p < hi) ? 2 : 1;
+#pragma nounroll
+    for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
+        if (r) __syncthreads();           // every wave is done with the first tile's LDS buffers
+        fwd_bf16_tile<D, NW, CAUSAL>(a, smem, bh, r ? p : hi);
+    }
+}
+
 template <int D, int NW, bool CAUSAL>
 int launch(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = NW * WQ;
@@ -415,7 +432,7 @@ int launch(const FwdArgs& a, hipStream_t stream) {
         attr_set = true;
     }
     const int n_qt = (a.N + BR - 1) / BR;
-    const int64_t grid = int64_t(n_qt) * a.B * a.H;
+    const int64_t grid = int64_t(CAUSAL ? (n_qt + 1) / 2 : n_qt) * a.B * a.H;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), LDS, stream, a);
     return static_cast<int>(hipGetLastError());
 }

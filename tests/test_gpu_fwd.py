@@ -72,7 +72,7 @@ def test_tiny_f32_workload(causal):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [1, 17, 64, 255, 600])
+@pytest.mark.parametrize("N", [1, 17, 64, 255, 600, 1000])
 def test_parity_full_compare(dtype, causal, d, N):
     dev, ref = _inputs(2, 3, N, d, 1000 + N + d, dtype)
     o, lse = _run(dev, causal)
