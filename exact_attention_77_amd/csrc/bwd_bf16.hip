@@ -151,249 +151,259 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // P^T then dS^T ([128 keys][64 queries] bf16 each).
     __shared__ __attribute__((aligned(1024))) char ptbuf[2 * PT_BYTES];
 
+    // Key tile kt meets the queries from kt*BK on (causal): a workgroup takes
+    // the pair (p, n_kt-1-p) of one head so that all carry the same work.
     const int BH = a.B * a.H;
-    const int kt = blockIdx.x / BH;     // key tile 0 (most queries) first
+    const int n_kt = (a.N + BK - 1) / BK;
+    const int kp = blockIdx.x / BH;
     const int bh = blockIdx.x % BH;
-    const int b = bh / a.H, h = bh % a.H;
-    const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
-    const u16* Qg = static_cast<const u16*>(a.q) + base;
-    const u16* Kg = static_cast<const u16*>(a.k) + base;
-    const u16* Vg = static_cast<const u16*>(a.v) + base;
-    const u16* Og = static_cast<const u16*>(a.dout) + base;
+    const int lo_kt = CAUSAL ? n_kt - 1 - kp : kp;
+    const int n_tiles = (CAUSAL && kp < lo_kt) ? 2 : 1;
+#pragma nounroll
+    for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
+        if (r) __syncthreads();           // every wave is done with the first tile's LDS
+        const int kt = r ? lo_kt : kp;
+        const int b = bh / a.H, h = bh % a.H;
+        const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
+        const u16* Qg = static_cast<const u16*>(a.q) + base;
+        const u16* Kg = static_cast<const u16*>(a.k) + base;
+        const u16* Vg = static_cast<const u16*>(a.v) + base;
+        const u16* Og = static_cast<const u16*>(a.dout) + base;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kb = wave & 3, qh = wave >> 2;
-    const int j = lane & 31, hh = lane >> 5;
-    const int k0 = kt * BK;
-    const int kw0 = k0 + 32 * kb;                 // first key of this wave
-    const int key = kw0 + j;                      // this lane's key
-    const int key_c = min(key, a.N - 1);          // rows past the end re-read the last row
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int kb = wave & 3, qh = wave >> 2;
+        const int j = lane & 31, hh = lane >> 5;
+        const int k0 = kt * BK;
+        const int kw0 = k0 + 32 * kb;                 // first key of this wave
+        const int key = kw0 + j;                      // this lane's key
+        const int key_c = min(key, a.N - 1);          // rows past the end re-read the last row
 
-    // ---- K tile -> LDS; V rows -> registers ----------------------------------
-#pragma unroll
-    for (int i = 0; i < NKB; ++i) {
-        const int blk = wave * NKB + i;
-        const int c = blk * 64 + lane;
-        const int row = c / CPR, pch = c % CPR;
-        const int64_t off = int64_t(min(k0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off), (lds_void*)(ktile + blk * 1024), 16, 0, 0);
-    }
-    // B operand of dO V^T: lane (key, half hh), k-step ks holds columns
-    // 16ks + 8hh .. +7 of the key's V row (K comes from the LDS tile).
-    bf16x8 vreg[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int64_t off = int64_t(key_c) * a.ss + 16 * ks + 8 * hh;
-        vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + off));
-    }
-
-    // ---- Q / dO / statistics tile copy (direct to LDS, swizzled rows) -------
-    auto copy_q = [&](int q0, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) {
-            const int blk = wave * NQB + i;
+        // ---- K tile -> LDS; V rows -> registers ----------------------------------
+    #pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+            const int blk = wave * NKB + i;
             const int c = blk * 64 + lane;
             const int row = c / CPR, pch = c % CPR;
-            const int64_t roff = int64_t(min(q0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(Qg + roff),
-                                             (lds_void*)((buf ? qtile1 : qtile0) + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(Og + roff),
-                                             (lds_void*)((buf ? otile1 : otile0) + blk * 1024), 16, 0, 0);
+            const int64_t off = int64_t(min(k0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
+            __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off), (lds_void*)(ktile + blk * 1024), 16, 0, 0);
         }
-        float* st = buf ? stat1 : stat0;
-        const int qq = min(q0 + lane, a.N - 1);
-        if (wave == 0)       // LSE*log2e of the 64 queries
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_lse2 + int64_t(bh) * a.N + qq),
-                                             (lds_void*)st, 4, 0, 0);
-        else if (wave == 1)  // -D
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_nd + int64_t(bh) * a.N + qq),
-                                             (lds_void*)(st + BQ), 4, 0, 0);
-    };
-
-    // ---- per-lane LDS offsets ----------------------------------------------
-    // Everything that varies with the buffer, the k-step or the 16-row block
-    // is a compile-time immediate; what remains is a handful of per-lane
-    // offsets (the XOR swizzles of rows 16c + r do not depend on c).
-    const int prow = 32 * qh + perm_row(j);                        // Q / dO row-operand row
-    const int krow = 32 * kb + j;                                  // K / P^T / dS^T row of this lane's key
-    const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
-    const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
-    const int tr_half = 8 * (lane & 1);
-    // P^T / dS^T: 128-byte rows (64 queries) of 8-byte pieces; the 16-byte
-    // chunk is XOR-swizzled by row so that per-key row reads (16 lanes, 16
-    // keys) and transposing reads (4 consecutive keys) are conflict-free.
-    auto pt_swz = [](int row) { return 2 * (4 * ((row >> 1) & 1) + ((row >> 2) & 3)); };
-    int qo[KS], ko[KS];           // row operands: Q/dO rows prow, K rows krow
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qo[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
-        ko[ks] = krow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(krow));
-    }
-    int tro[DT][2];               // transposed reads, rows tr_row (+4) of column block dt
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int r = tr_row + 4 * e;
-            tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
+        // B operand of dO V^T: lane (key, half hh), k-step ks holds columns
+        // 16ks + 8hh .. +7 of the key's V row (K comes from the LDS tile).
+        bf16x8 vreg[KS];
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int64_t off = int64_t(key_c) * a.ss + 16 * ks + 8 * hh;
+            vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + off));
         }
-    int pto[BQ / 16];             // P^T row reads (dS^T: + PT_BYTES)
-#pragma unroll
-    for (int c = 0; c < BQ / 16; ++c) pto[c] = krow * 128 + 8 * ((4 * c + 2 * hh) ^ pt_swz(krow));
-    // P^T row writes (dS^T: + PT_BYTES): 16 bytes = queries 32qh + 16c + 8hh .. +7
-    // (the swizzle is even, so pieces p and p + 1 stay adjacent and in order)
-    int pwo[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) pwo[c] = krow * 128 + 8 * ((8 * qh + 4 * c + 2 * hh) ^ pt_swz(krow));
-    auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
-    auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
 
-    f32x16 acc[DT];   // dV^T (qh = 0) or dK^T (qh = 1) of this wave's 32 keys
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
-
-    const float c2 = a.scale_log2;
-    const int n_qt = (a.N + BQ - 1) / BQ;
-    const int qt0 = CAUSAL ? k0 / BQ : 0;
-
-    if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
-    // One query tile; `bufc` carries the LDS buffer as a compile-time constant
-    // (the loop below is unrolled by two) so that the compiler can tell the
-    // prefetch target from the buffer being read and does not wait for it.
-    auto step = [&](int it, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        const int qt_base = it * BQ;
-        const int q0 = qt_base + 32 * qh;         // first query of this wave
-        // tile `it` is in LDS; every wave is done with the previous P^T / dS^T
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-        const char* qt = buf ? qtile1 : qtile0;
-        const char* ot = buf ? otile1 : otile0;
-        const float* ls = (buf ? stat1 : stat0) + 32 * qh;
-
-        // S = Q K^T and dP - D (register g = 4r + t of lane half hh: query
-        // q0 + 16(r>>1) + 8hh + 4(r&1) + t, key `key`)
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float4 nd = *reinterpret_cast<const float4*>(ls + BQ + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
-            dp[4 * r + 0] = nd.x; dp[4 * r + 1] = nd.y; dp[4 * r + 2] = nd.z; dp[4 * r + 3] = nd.w;
-        }
-#pragma unroll
-        for (int g = 0; g < 16; ++g) s[g] = 0.f;
-        {   // 2*KS products alternating S / dP - D; LDS operands read two ahead
-            auto srcA = [&](int m) { return ld16((m & 1) ? ot : qt, qo[m >> 1]); };
-            bf16x8 opA[3], opK[3];
-            opA[0] = srcA(0); opK[0] = ld16(ktile, ko[0]);
-            opA[1] = srcA(1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = 0; m < 2 * KS; ++m) {
-                if (m + 2 < 2 * KS) {
-                    opA[(m + 2) % 3] = srcA(m + 2);
-                    if (!(m & 1)) opK[(m + 2) % 3] = ld16(ktile, ko[(m + 2) >> 1]);
-                }
-                if (m & 1)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], vreg[m >> 1], dp, 0, 0, 0);
-                else
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], opK[m % 3], s, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+        // ---- Q / dO / statistics tile copy (direct to LDS, swizzled rows) -------
+        auto copy_q = [&](int q0, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+    #pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int blk = wave * NQB + i;
+                const int c = blk * 64 + lane;
+                const int row = c / CPR, pch = c % CPR;
+                const int64_t roff = int64_t(min(q0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(Qg + roff),
+                                                 (lds_void*)((buf ? qtile1 : qtile0) + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(Og + roff),
+                                                 (lds_void*)((buf ? otile1 : otile0) + blk * 1024), 16, 0, 0);
             }
-        }
-
-        // P = exp2(S c - LSE log2 e), zero for masked (query, key) pairs
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float4 l2 = *reinterpret_cast<const float4*>(ls + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
-            p[4 * r + 0] = fmaf(s[4 * r + 0], c2, -l2.x);
-            p[4 * r + 1] = fmaf(s[4 * r + 1], c2, -l2.y);
-            p[4 * r + 2] = fmaf(s[4 * r + 2], c2, -l2.z);
-            p[4 * r + 3] = fmaf(s[4 * r + 3], c2, -l2.w);
-        }
-        const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 32 > a.N || kw0 + 32 > a.N;
-        if (edge) {  // wave-uniform: diagonal or ragged blocks only
-            const int lo = CAUSAL ? key - q0 - 8 * hh : -(1 << 30);
-            const int hi = key < a.N ? a.N - 1 - q0 - 8 * hh : -1;
-#pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                const int r = g >> 2, t = g & 3;
-                const int off = 16 * (r >> 1) + 4 * (r & 1) + t;
-                if (off < lo || off > hi) p[g] = -INFINITY;
-            }
-        }
-        // P and dS = P (dP - D) as bf16, stored transposed (row = key) for the
-        // products over the whole 64-query tile
-        bf16x8 pb[2], dsb[2];
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            p[g] = __builtin_amdgcn_exp2f(p[g]);
-            pb[g >> 3][g & 7] = static_cast<__bf16>(p[g]);
-            dsb[g >> 3][g & 7] = static_cast<__bf16>(p[g] * dp[g]);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            *reinterpret_cast<bf16x8*>(ptbuf + pwo[c]) = pb[c];
-            *reinterpret_cast<bf16x8*>(ptbuf + pwo[c] + PT_BYTES) = dsb[c];
-        }
-        // Prefetch the next tile once this iteration's LDS stores are issued
-        // (LDS stores behind a pending direct-to-LDS load get made to wait).
-        if (it + 1 < n_qt) copy_q(qt_base + BQ, std::integral_constant<int, buf ^ 1>{});
-        // P^T and dS^T of the whole tile are in LDS (LDS stores only: the
-        // prefetch just issued stays in flight across this barrier)
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        __builtin_amdgcn_s_barrier();
-
-        // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1), over 64 queries
-        auto tile_product = [&](const char* at, auto bo) {
-            constexpr int BO = decltype(bo)::value;
-            constexpr int NP = BQ / 16 * DT;   // products; A operands read two ahead
-            auto src = [&](int n) {
-                const int c = n / DT, dt = n % DT;
-                return ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
-            };
-            bf16x8 op[3], bop = ld16(ptbuf, pto[0] + BO);
-            op[0] = src(0);
-            op[1] = src(1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = 0; n < NP; ++n) {
-                if (n + 2 < NP) op[(n + 2) % 3] = src(n + 2);
-                const int c = n / DT, dt = n % DT;
-                const bf16x8 b = bop;
-                if (dt == DT - 1 && c + 1 < BQ / 16) bop = ld16(ptbuf, pto[c + 1] + BO);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], b, acc[dt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            float* st = buf ? stat1 : stat0;
+            const int qq = min(q0 + lane, a.N - 1);
+            if (wave == 0)       // LSE*log2e of the 64 queries
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_lse2 + int64_t(bh) * a.N + qq),
+                                                 (lds_void*)st, 4, 0, 0);
+            else if (wave == 1)  // -D
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_nd + int64_t(bh) * a.N + qq),
+                                                 (lds_void*)(st + BQ), 4, 0, 0);
         };
-        if (qh) tile_product(qt, std::integral_constant<int, PT_BYTES>{});
-        else    tile_product(ot, std::integral_constant<int, 0>{});
 
-    };
-    for (int it = qt0; it < n_qt; it += 2) {
-        step(it, std::integral_constant<int, 0>{});
-        if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
-    }
-
-    // ---- epilogue: dV (qh = 0) or dK = scale * (dK^T)^T (qh = 1), bf16 -------
-    // register g of lane half hh: column 32dt + 8(g>>2) + 4hh + (g&3) of key `key`
-    if (key < a.N) {
-        u16* row = static_cast<u16*>(qh ? a.dk : a.dv) + base + int64_t(key) * a.ss;
-        const float f = qh ? a.scale : 1.0f;
-#pragma unroll
+        // ---- per-lane LDS offsets ----------------------------------------------
+        // Everything that varies with the buffer, the k-step or the 16-row block
+        // is a compile-time immediate; what remains is a handful of per-lane
+        // offsets (the XOR swizzles of rows 16c + r do not depend on c).
+        const int prow = 32 * qh + perm_row(j);                        // Q / dO row-operand row
+        const int krow = 32 * kb + j;                                  // K / P^T / dS^T row of this lane's key
+        const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
+        const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
+        const int tr_half = 8 * (lane & 1);
+        // P^T / dS^T: 128-byte rows (64 queries) of 8-byte pieces; the 16-byte
+        // chunk is XOR-swizzled by row so that per-key row reads (16 lanes, 16
+        // keys) and transposing reads (4 consecutive keys) are conflict-free.
+        auto pt_swz = [](int row) { return 2 * (4 * ((row >> 1) & 1) + ((row >> 2) & 3)); };
+        int qo[KS], ko[KS];           // row operands: Q/dO rows prow, K rows krow
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qo[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
+            ko[ks] = krow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(krow));
+        }
+        int tro[DT][2];               // transposed reads, rows tr_row (+4) of column block dt
+    #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                __bf16 x4[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * f);
-                *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
+    #pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = tr_row + 4 * e;
+                tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
             }
+        int pto[BQ / 16];             // P^T row reads (dS^T: + PT_BYTES)
+    #pragma unroll
+        for (int c = 0; c < BQ / 16; ++c) pto[c] = krow * 128 + 8 * ((4 * c + 2 * hh) ^ pt_swz(krow));
+        // P^T row writes (dS^T: + PT_BYTES): 16 bytes = queries 32qh + 16c + 8hh .. +7
+        // (the swizzle is even, so pieces p and p + 1 stay adjacent and in order)
+        int pwo[2];
+    #pragma unroll
+        for (int c = 0; c < 2; ++c) pwo[c] = krow * 128 + 8 * ((8 * qh + 4 * c + 2 * hh) ^ pt_swz(krow));
+        auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
+        auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
+
+        f32x16 acc[DT];   // dV^T (qh = 0) or dK^T (qh = 1) of this wave's 32 keys
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
+
+        const float c2 = a.scale_log2;
+        const int n_qt = (a.N + BQ - 1) / BQ;
+        const int qt0 = CAUSAL ? k0 / BQ : 0;
+
+        if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
+        // One query tile; `bufc` carries the LDS buffer as a compile-time constant
+        // (the loop below is unrolled by two) so that the compiler can tell the
+        // prefetch target from the buffer being read and does not wait for it.
+        auto step = [&](int it, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+            const int qt_base = it * BQ;
+            const int q0 = qt_base + 32 * qh;         // first query of this wave
+            // tile `it` is in LDS; every wave is done with the previous P^T / dS^T
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            const char* qt = buf ? qtile1 : qtile0;
+            const char* ot = buf ? otile1 : otile0;
+            const float* ls = (buf ? stat1 : stat0) + 32 * qh;
+
+            // S = Q K^T and dP - D (register g = 4r + t of lane half hh: query
+            // q0 + 16(r>>1) + 8hh + 4(r&1) + t, key `key`)
+            f32x16 s, dp;
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4 nd = *reinterpret_cast<const float4*>(ls + BQ + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
+                dp[4 * r + 0] = nd.x; dp[4 * r + 1] = nd.y; dp[4 * r + 2] = nd.z; dp[4 * r + 3] = nd.w;
+            }
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) s[g] = 0.f;
+            {   // 2*KS products alternating S / dP - D; LDS operands read two ahead
+                auto srcA = [&](int m) { return ld16((m & 1) ? ot : qt, qo[m >> 1]); };
+                bf16x8 opA[3], opK[3];
+                opA[0] = srcA(0); opK[0] = ld16(ktile, ko[0]);
+                opA[1] = srcA(1);
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int m = 0; m < 2 * KS; ++m) {
+                    if (m + 2 < 2 * KS) {
+                        opA[(m + 2) % 3] = srcA(m + 2);
+                        if (!(m & 1)) opK[(m + 2) % 3] = ld16(ktile, ko[(m + 2) >> 1]);
+                    }
+                    if (m & 1)
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], vreg[m >> 1], dp, 0, 0, 0);
+                    else
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], opK[m % 3], s, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // P = exp2(S c - LSE log2 e), zero for masked (query, key) pairs
+            float p[16];
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4 l2 = *reinterpret_cast<const float4*>(ls + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
+                p[4 * r + 0] = fmaf(s[4 * r + 0], c2, -l2.x);
+                p[4 * r + 1] = fmaf(s[4 * r + 1], c2, -l2.y);
+                p[4 * r + 2] = fmaf(s[4 * r + 2], c2, -l2.z);
+                p[4 * r + 3] = fmaf(s[4 * r + 3], c2, -l2.w);
+            }
+            const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 32 > a.N || kw0 + 32 > a.N;
+            if (edge) {  // wave-uniform: diagonal or ragged blocks only
+                const int lo = CAUSAL ? key - q0 - 8 * hh : -(1 << 30);
+                const int hi = key < a.N ? a.N - 1 - q0 - 8 * hh : -1;
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    const int r = g >> 2, t = g & 3;
+                    const int off = 16 * (r >> 1) + 4 * (r & 1) + t;
+                    if (off < lo || off > hi) p[g] = -INFINITY;
+                }
+            }
+            // P and dS = P (dP - D) as bf16, stored transposed (row = key) for the
+            // products over the whole 64-query tile
+            bf16x8 pb[2], dsb[2];
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                p[g] = __builtin_amdgcn_exp2f(p[g]);
+                pb[g >> 3][g & 7] = static_cast<__bf16>(p[g]);
+                dsb[g >> 3][g & 7] = static_cast<__bf16>(p[g] * dp[g]);
+            }
+    #pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                *reinterpret_cast<bf16x8*>(ptbuf + pwo[c]) = pb[c];
+                *reinterpret_cast<bf16x8*>(ptbuf + pwo[c] + PT_BYTES) = dsb[c];
+            }
+            // Prefetch the next tile once this iteration's LDS stores are issued
+            // (LDS stores behind a pending direct-to-LDS load get made to wait).
+            if (it + 1 < n_qt) copy_q(qt_base + BQ, std::integral_constant<int, buf ^ 1>{});
+            // P^T and dS^T of the whole tile are in LDS (LDS stores only: the
+            // prefetch just issued stays in flight across this barrier)
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            __builtin_amdgcn_s_barrier();
+
+            // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1), over 64 queries
+            auto tile_product = [&](const char* at, auto bo) {
+                constexpr int BO = decltype(bo)::value;
+                constexpr int NP = BQ / 16 * DT;   // products; A operands read two ahead
+                auto src = [&](int n) {
+                    const int c = n / DT, dt = n % DT;
+                    return ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
+                };
+                bf16x8 op[3], bop = ld16(ptbuf, pto[0] + BO);
+                op[0] = src(0);
+                op[1] = src(1);
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int n = 0; n < NP; ++n) {
+                    if (n + 2 < NP) op[(n + 2) % 3] = src(n + 2);
+                    const int c = n / DT, dt = n % DT;
+                    const bf16x8 b = bop;
+                    if (dt == DT - 1 && c + 1 < BQ / 16) bop = ld16(ptbuf, pto[c + 1] + BO);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], b, acc[dt], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (qh) tile_product(qt, std::integral_constant<int, PT_BYTES>{});
+            else    tile_product(ot, std::integral_constant<int, 0>{});
+
+        };
+        for (int it = qt0; it < n_qt; it += 2) {
+            step(it, std::integral_constant<int, 0>{});
+            if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
+        }
+
+        // ---- epilogue: dV (qh = 0) or dK = scale * (dK^T)^T (qh = 1), bf16 -------
+        // register g of lane half hh: column 32dt + 8(g>>2) + 4hh + (g&3) of key `key`
+        if (key < a.N) {
+            u16* row = static_cast<u16*>(qh ? a.dk : a.dv) + base + int64_t(key) * a.ss;
+            const float f = qh ? a.scale : 1.0f;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    __bf16 x4[4];
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * f);
+                    *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
+                }
+        }
     }
 }
 
@@ -411,184 +421,191 @@ void bwd_dq_kernel(BwdArgs a) {
     static_assert(NI >= 1, "tile shape");
     __shared__ __attribute__((aligned(1024))) char ktile0[TB], ktile1[TB], vtile0[TB], vtile1[TB];
 
-    // ---- work decomposition: heaviest query tiles first, one head per XCD ----
+    // ---- work decomposition: one head per XCD; under the causal mask a
+    // workgroup takes the query-tile pair (T-1-p, p), equal work for all ----
     const int n_qt = (a.N + BR - 1) / BR;
-    const int total = n_qt * a.B * a.H;
+    const int per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+    const int total = per_head * a.B * a.H;
     int id = blockIdx.x;
     if ((total & 7) == 0) {
         const int per = total >> 3;
         id = (id & 7) * per + (id >> 3);
     }
-    const int bh = id / n_qt;
-    int qt = id % n_qt;
-    if (CAUSAL) qt = n_qt - 1 - qt;
-    const int b = bh / a.H, h = bh % a.H;
-    const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
-    const u16* Qg = static_cast<const u16*>(a.q) + base;
-    const u16* Kg = static_cast<const u16*>(a.k) + base;
-    const u16* Vg = static_cast<const u16*>(a.v) + base;
-    const u16* Og = static_cast<const u16*>(a.dout) + base;
+    const int bh = id / per_head, p = id % per_head;
+    const int hi = CAUSAL ? n_qt - 1 - p : p;
+    const int n_tiles = (CAUSAL && p < hi) ? 2 : 1;
+#pragma nounroll
+    for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
+        if (r) __syncthreads();           // every wave is done with the first tile's LDS
+        const int qt = r ? p : hi;
+        const int b = bh / a.H, h = bh % a.H;
+        const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
+        const u16* Qg = static_cast<const u16*>(a.q) + base;
+        const u16* Kg = static_cast<const u16*>(a.k) + base;
+        const u16* Vg = static_cast<const u16*>(a.v) + base;
+        const u16* Og = static_cast<const u16*>(a.dout) + base;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 31, hh = lane >> 5;
-    const int q0 = qt * BR + 32 * wave;         // first query of this wave
-    const int qi = q0 + j;                      // this lane's query
-    const int n_kt = (a.N + BC - 1) / BC;
-    const int nt = CAUSAL ? min(n_kt, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt;
-    int wnt = CAUSAL ? min(nt, (min(a.N, q0 + 32) + BC - 1) / BC) : nt;
-    if (q0 >= a.N) wnt = 0;
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int j = lane & 31, hh = lane >> 5;
+        const int q0 = qt * BR + 32 * wave;         // first query of this wave
+        const int qi = q0 + j;                      // this lane's query
+        const int n_kt = (a.N + BC - 1) / BC;
+        const int nt = CAUSAL ? min(n_kt, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt;
+        int wnt = CAUSAL ? min(nt, (min(a.N, q0 + 32) + BC - 1) / BC) : nt;
+        if (q0 >= a.N) wnt = 0;
 
-    // ---- K/V tile copy (direct to LDS, swizzled rows; rows past the end
-    // re-read the last row, their scores are masked) ---------------------------
-    auto copy_kv = [&](int kt, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int blk = wave * NI + i;
-            const int c = blk * 64 + lane;
-            const int row = c / CPR, pch = c % CPR;
-            const int64_t off = int64_t(min(kt * BC + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off),
-                                             (lds_void*)((buf ? ktile1 : ktile0) + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(Vg + off),
-                                             (lds_void*)((buf ? vtile1 : vtile0) + blk * 1024), 16, 0, 0);
+        // ---- K/V tile copy (direct to LDS, swizzled rows; rows past the end
+        // re-read the last row, their scores are masked) ---------------------------
+        auto copy_kv = [&](int kt, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+    #pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int blk = wave * NI + i;
+                const int c = blk * 64 + lane;
+                const int row = c / CPR, pch = c % CPR;
+                const int64_t off = int64_t(min(kt * BC + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off),
+                                                 (lds_void*)((buf ? ktile1 : ktile0) + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(Vg + off),
+                                                 (lds_void*)((buf ? vtile1 : vtile0) + blk * 1024), 16, 0, 0);
+            }
+        };
+
+        // ---- per-query operands and statistics (zero past the end) --------------
+        bf16x8 qreg[KS], oreg[KS];   // B operands of K Q^T / V dO^T: lane (query, half hh)
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 xq = make_uint4(0, 0, 0, 0), xo = make_uint4(0, 0, 0, 0);
+            if (qi < a.N) {
+                const int64_t off = int64_t(qi) * a.ss + 16 * ks + 8 * hh;
+                xq = *reinterpret_cast<const uint4*>(Qg + off);
+                xo = *reinterpret_cast<const uint4*>(Og + off);
+            }
+            qreg[ks] = __builtin_bit_cast(bf16x8, xq);
+            oreg[ks] = __builtin_bit_cast(bf16x8, xo);
         }
-    };
+        const float lse2 = qi < a.N ? a.ws_lse2[int64_t(bh) * a.N + qi] : 0.f;
+        const float nd = qi < a.N ? a.ws_nd[int64_t(bh) * a.N + qi] : 0.f;
 
-    // ---- per-query operands and statistics (zero past the end) --------------
-    bf16x8 qreg[KS], oreg[KS];   // B operands of K Q^T / V dO^T: lane (query, half hh)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 xq = make_uint4(0, 0, 0, 0), xo = make_uint4(0, 0, 0, 0);
-        if (qi < a.N) {
-            const int64_t off = int64_t(qi) * a.ss + 16 * ks + 8 * hh;
-            xq = *reinterpret_cast<const uint4*>(Qg + off);
-            xo = *reinterpret_cast<const uint4*>(Og + off);
-        }
-        qreg[ks] = __builtin_bit_cast(bf16x8, xq);
-        oreg[ks] = __builtin_bit_cast(bf16x8, xo);
-    }
-    const float lse2 = qi < a.N ? a.ws_lse2[int64_t(bh) * a.N + qi] : 0.f;
-    const float nd = qi < a.N ? a.ws_nd[int64_t(bh) * a.N + qi] : 0.f;
+        // ---- per-lane LDS offsets ----------------------------------------------
+        const int prow = perm_row(j);                                  // K / V row operand (+32 st)
+        const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
+        const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
+        const int tr_half = 8 * (lane & 1);
+        int ro[KS];
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ro[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
+        int tro[DT][2];
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = tr_row + 4 * e;
+                tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
+            }
+        auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
+        auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
 
-    // ---- per-lane LDS offsets ----------------------------------------------
-    const int prow = perm_row(j);                                  // K / V row operand (+32 st)
-    const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
-    const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
-    const int tr_half = 8 * (lane & 1);
-    int ro[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ro[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
-    int tro[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int r = tr_row + 4 * e;
-            tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
-        }
-    auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
-    auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
+        f32x16 acc[DT];   // dQ^T: register g of lane half hh holds column 32dt + 8(g>>2) + 4hh + (g&3)
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
+        const float c2 = a.scale_log2;
 
-    f32x16 acc[DT];   // dQ^T: register g of lane half hh holds column 32dt + 8(g>>2) + 4hh + (g&3)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
-    const float c2 = a.scale_log2;
-
-    // One key tile, in 64-key blocks: per 32-key subtile st, S^T and dP^T - D,
-    // then P^T and dS^T; register g = 4r + t of lane half hh holds key
-    // 32st + 16(r>>1) + 8hh + 4(r&1) + t of the block, so the bf16 dS^T
-    // registers are the B operand of the block's 16-key chunk c = 2st + (r>>1).
-    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < BC / 64; ++kb) {
-            const int k_lo = kt * BC + 64 * kb;
-            if (CAUSAL && kb > 0 && k_lo > q0 + 31) continue;   // wave-uniform: block fully masked
-            const bool edge = (k_lo + 64 > a.N) || (CAUSAL && k_lo + 63 > q0);
-            const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 8 * hh;
-            const char* kb_lds = kt_lds + 64 * kb * 2 * D;
-            const char* vb_lds = vt_lds + 64 * kb * 2 * D;
-            bf16x8 dsb[2][2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                f32x16 s, dp;
-#pragma unroll
-                for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
-                // 2*KS products alternating S^T / dP^T; LDS operands read two ahead
-                auto src = [&](int m) {
-                    return ld16((m & 1) ? vb_lds : kb_lds, 32 * st * 2 * D + ro[m >> 1]);
+        // One key tile, in 64-key blocks: per 32-key subtile st, S^T and dP^T - D,
+        // then P^T and dS^T; register g = 4r + t of lane half hh holds key
+        // 32st + 16(r>>1) + 8hh + 4(r&1) + t of the block, so the bf16 dS^T
+        // registers are the B operand of the block's 16-key chunk c = 2st + (r>>1).
+        auto compute = [&](int kt, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
+    #pragma unroll
+            for (int kb = 0; kb < BC / 64; ++kb) {
+                const int k_lo = kt * BC + 64 * kb;
+                if (CAUSAL && kb > 0 && k_lo > q0 + 31) continue;   // wave-uniform: block fully masked
+                const bool edge = (k_lo + 64 > a.N) || (CAUSAL && k_lo + 63 > q0);
+                const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 8 * hh;
+                const char* kb_lds = kt_lds + 64 * kb * 2 * D;
+                const char* vb_lds = vt_lds + 64 * kb * 2 * D;
+                bf16x8 dsb[2][2];
+    #pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    f32x16 s, dp;
+    #pragma unroll
+                    for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
+                    // 2*KS products alternating S^T / dP^T; LDS operands read two ahead
+                    auto src = [&](int m) {
+                        return ld16((m & 1) ? vb_lds : kb_lds, 32 * st * 2 * D + ro[m >> 1]);
+                    };
+                    bf16x8 op[3];
+                    op[0] = src(0);
+                    op[1] = src(1);
+    #pragma unroll
+                    for (int m = 0; m < 2 * KS; ++m) {
+                        if (m + 2 < 2 * KS) op[(m + 2) % 3] = src(m + 2);
+                        if (m & 1)
+                            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], oreg[m >> 1], dp, 0, 0, 0);
+                        else
+                            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], qreg[m >> 1], s, 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+    #pragma unroll
+                    for (int g = 0; g < 16; ++g) {
+                        float x = fmaf(s[g], c2, -lse2);
+                        if (edge) {
+                            const int r = g >> 2, t = g & 3;
+                            if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) x = -INFINITY;
+                        }
+                        dsb[st][g >> 3][g & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x) * dp[g]);
+                    }
+                }
+                // dQ^T += K^T dS^T over the block's four 16-key chunks (operands two ahead)
+                constexpr int NQ = 4 * DT;
+                auto tsrc = [&](int n) {
+                    const int c = n / DT, dt = n % DT;
+                    return ldtr(kb_lds, 16 * c * 2 * D + tro[dt][0], 16 * c * 2 * D + tro[dt][1]);
                 };
-                bf16x8 op[3];
-                op[0] = src(0);
-                op[1] = src(1);
-#pragma unroll
-                for (int m = 0; m < 2 * KS; ++m) {
-                    if (m + 2 < 2 * KS) op[(m + 2) % 3] = src(m + 2);
-                    if (m & 1)
-                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], oreg[m >> 1], dp, 0, 0, 0);
-                    else
-                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], qreg[m >> 1], s, 0, 0, 0);
+                bf16x8 top[3];
+                top[0] = tsrc(0);
+                top[1] = tsrc(1);
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int n = 0; n < NQ; ++n) {
+                    if (n + 2 < NQ) top[(n + 2) % 3] = tsrc(n + 2);
+                    const int c = n / DT, dt = n % DT;
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[n % 3], dsb[c >> 1][c & 1], acc[dt], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int g = 0; g < 16; ++g) {
-                    float x = fmaf(s[g], c2, -lse2);
-                    if (edge) {
-                        const int r = g >> 2, t = g & 3;
-                        if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) x = -INFINITY;
-                    }
-                    dsb[st][g >> 3][g & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x) * dp[g]);
-                }
             }
-            // dQ^T += K^T dS^T over the block's four 16-key chunks (operands two ahead)
-            constexpr int NQ = 4 * DT;
-            auto tsrc = [&](int n) {
-                const int c = n / DT, dt = n % DT;
-                return ldtr(kb_lds, 16 * c * 2 * D + tro[dt][0], 16 * c * 2 * D + tro[dt][1]);
-            };
-            bf16x8 top[3];
-            top[0] = tsrc(0);
-            top[1] = tsrc(1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = 0; n < NQ; ++n) {
-                if (n + 2 < NQ) top[(n + 2) % 3] = tsrc(n + 2);
-                const int c = n / DT, dt = n % DT;
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[n % 3], dsb[c >> 1][c & 1], acc[dt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        };
+
+        if (nt > 0) copy_kv(0, std::integral_constant<int, 0>{});
+        auto step = [&](int kt, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();   // tile kt is in LDS; everyone is done with tile kt - 1
+            if (kt + 1 < nt) copy_kv(kt + 1, std::integral_constant<int, buf ^ 1>{});
+            if (kt < wnt) compute(kt, buf ? ktile1 : ktile0, buf ? vtile1 : vtile0);
+        };
+        for (int kt = 0; kt < nt; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            if (kt + 1 < nt) step(kt + 1, std::integral_constant<int, 1>{});
         }
-    };
 
-    if (nt > 0) copy_kv(0, std::integral_constant<int, 0>{});
-    auto step = [&](int kt, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();   // tile kt is in LDS; everyone is done with tile kt - 1
-        if (kt + 1 < nt) copy_kv(kt + 1, std::integral_constant<int, buf ^ 1>{});
-        if (kt < wnt) compute(kt, buf ? ktile1 : ktile0, buf ? vtile1 : vtile0);
-    };
-    for (int kt = 0; kt < nt; kt += 2) {
-        step(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < nt) step(kt + 1, std::integral_constant<int, 1>{});
-    }
-
-    // ---- epilogue: dQ = scale * (dQ^T)^T, bf16 -------------------------------
-    if (qi < a.N) {
-        u16* row = static_cast<u16*>(a.dq) + base + int64_t(qi) * a.ss;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                __bf16 x4[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * a.scale);
-                *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
-            }
+        // ---- epilogue: dQ = scale * (dQ^T)^T, bf16 -------------------------------
+        if (qi < a.N) {
+            u16* row = static_cast<u16*>(a.dq) + base + int64_t(qi) * a.ss;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    __bf16 x4[4];
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * a.scale);
+                    *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
+                }
+        }
     }
 }
 
@@ -598,12 +615,14 @@ int run(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
     int err = static_cast<int>(hipGetLastError());
     if (err) return err;
-    const unsigned g_kv = static_cast<unsigned>(int64_t((a.N + BK - 1) / BK) * a.B * a.H);
+    const int n_kt = (a.N + BK - 1) / BK;
+    const unsigned g_kv = static_cast<unsigned>(int64_t(a.causal ? (n_kt + 1) / 2 : n_kt) * a.B * a.H);
     if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(512), 0, s, a);
     if ((err = static_cast<int>(hipGetLastError()))) return err;
     constexpr int NW = 8, BC = 128;   // dQ kernel: 256 queries per workgroup, 128-key tiles
-    const unsigned g_q = static_cast<unsigned>(int64_t((a.N + 32 * NW - 1) / (32 * NW)) * a.B * a.H);
+    const int n_qt = (a.N + 32 * NW - 1) / (32 * NW);
+    const unsigned g_q = static_cast<unsigned>(int64_t(a.causal ? (n_qt + 1) / 2 : n_qt) * a.B * a.H);
     if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
     else hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
     return static_cast<int>(hipGetLastError());
