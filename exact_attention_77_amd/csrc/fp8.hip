@@ -219,197 +219,205 @@ void fwd_fp8_kernel(Fp8Args a) {
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
+    // One head per XCD; under the causal mask a workgroup takes the query-tile
+    // pair (T-1-p, p), so that all workgroups carry the same work.
     const int n_qt = (a.N + BR - 1) / BR;
-    const int total = n_qt * a.B * a.H;
+    const int per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+    const int total = per_head * a.B * a.H;
     int id = blockIdx.x;
     if ((total & 7) == 0) {
         const int per = total >> 3;
         id = (id & 7) * per + (id >> 3);
     }
-    const int bh = id / n_qt;
-    int qt = id % n_qt;
-    if (CAUSAL) qt = n_qt - 1 - qt;
-    const int b = bh / a.H, h = bh % a.H;
-    const int64_t npad = fp8_npad(a.N);
-    const uint8_t* Qg = a.q + int64_t(bh) * a.N * D;
-    const uint8_t* Kg = a.k + int64_t(bh) * a.N * D;
-    const uint8_t* Vg = a.vt + int64_t(bh) * D * npad;
-    uint16_t* Og = static_cast<uint16_t*>(a.o) + int64_t(b) * a.osb + int64_t(h) * a.osh;
-    const int nqb = (a.N + kQBlk - 1) / kQBlk, nkb = (a.N + kKBlk - 1) / kKBlk;
-    const int nvb = (a.N + kVBlk - 1) / kVBlk;
+    const int bh = id / per_head, p = id % per_head;
+    const int hi = CAUSAL ? n_qt - 1 - p : p;
+    const int n_tiles = (CAUSAL && p < hi) ? 2 : 1;
+#pragma nounroll
+    for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
+        if (r) __syncthreads();           // every wave is done with the first tile's LDS
+        const int qt = r ? p : hi;
+        const int b = bh / a.H, h = bh % a.H;
+        const int64_t npad = fp8_npad(a.N);
+        const uint8_t* Qg = a.q + int64_t(bh) * a.N * D;
+        const uint8_t* Kg = a.k + int64_t(bh) * a.N * D;
+        const uint8_t* Vg = a.vt + int64_t(bh) * D * npad;
+        uint16_t* Og = static_cast<uint16_t*>(a.o) + int64_t(b) * a.osb + int64_t(h) * a.osh;
+        const int nqb = (a.N + kQBlk - 1) / kQBlk, nkb = (a.N + kKBlk - 1) / kKBlk;
+        const int nvb = (a.N + kVBlk - 1) / kVBlk;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 31, hh = lane >> 5;
-    const int q0 = qt * BR + wave * WQ;
-    const int qi = q0 + j;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int j = lane & 31, hh = lane >> 5;
+        const int q0 = qt * BR + wave * WQ;
+        const int qi = q0 + j;
 
-    const int n_kt_all = (a.N + BC - 1) / BC;
-    const int nt = CAUSAL ? min(n_kt_all, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt_all;
-    int wnt = CAUSAL ? min(nt, (min(a.N, q0 + WQ) + BC - 1) / BC) : nt;
-    if (q0 >= a.N) wnt = 0;
+        const int n_kt_all = (a.N + BC - 1) / BC;
+        const int nt = CAUSAL ? min(n_kt_all, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt_all;
+        int wnt = CAUSAL ? min(nt, (min(a.N, q0 + WQ) + BC - 1) / BC) : nt;
+        if (q0 >= a.N) wnt = 0;
 
-    // direct global -> LDS copies (1 KB per wave instruction, XOR-swizzled rows)
-    auto copy_k = [&](int kt, int off) {
-        for (int bk = wave; bk < NBK; bk += NW) {
-            const int c = bk * 64 + lane;
-            const int row = c / TL::KCPR, pch = c % TL::KCPR;
-            const int key = min(kt * BC + row, a.N - 1);
-            const uint8_t* g = Kg + int64_t(key) * D + 16 * (pch ^ TL::kswz(row));
-            __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
-        }
-    };
-    auto copy_v = [&](int kt, int off) {
-        for (int bk = wave; bk < NBV; bk += NW) {
-            const int c = bk * 64 + lane;
-            const int row = c / 4, pch = c % 4;  // row = head-dim index
-            const uint8_t* g = Vg + int64_t(row) * npad + int64_t(kt) * BC + 16 * (pch ^ TL::vswz(row));
-            __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
-        }
-    };
-    constexpr int K_OFF0 = 0, K_OFF1 = TL::KBYTES, V_OFF0 = 2 * TL::KBYTES, V_OFF1 = 2 * TL::KBYTES + TL::VBYTES;
-
-    // Q^T operand: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31]
-    i32x8 qreg[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-        if (qi < a.N) {
-            const uint8_t* p = Qg + int64_t(qi) * D + 64 * ks + 32 * hh;
-            lo = *reinterpret_cast<const uint4*>(p);
-            hi = *reinterpret_cast<const uint4*>(p + 16);
-        }
-        qreg[ks] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    }
-    const float sq = (q0 < a.N) ? a.qs[int64_t(bh) * nqb + q0 / kQBlk] : 1.f;
-    const float c2q = a.scale_log2 * sq;
-
-    f32x16 oacc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 16; ++g) oacc[dt][g] = 0.f;
-    float m_ref = -FLT_MAX;  // log2 units of the true scaled score
-    float lsum = 0.f;        // this lane's share of sum(256 p)
-
-    auto scores = [&](f32x16 (&s)[2], const char* kt_lds) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
-            const int row = krow8(j, st);
-            const char* rp = kt_lds + row * D;
-            const int sw = TL::kswz(row);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh) ^ sw));
-                const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh + 1) ^ sw));
-                const i32x8 ka = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-                s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qreg[ks], s[st], 0, 0, 0, 127, 0, 127);
+        // direct global -> LDS copies (1 KB per wave instruction, XOR-swizzled rows)
+        auto copy_k = [&](int kt, int off) {
+            for (int bk = wave; bk < NBK; bk += NW) {
+                const int c = bk * 64 + lane;
+                const int row = c / TL::KCPR, pch = c % TL::KCPR;
+                const int key = min(kt * BC + row, a.N - 1);
+                const uint8_t* g = Kg + int64_t(key) * D + 16 * (pch ^ TL::kswz(row));
+                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
             }
-        }
-    };
+        };
+        auto copy_v = [&](int kt, int off) {
+            for (int bk = wave; bk < NBV; bk += NW) {
+                const int c = bk * 64 + lane;
+                const int row = c / 4, pch = c % 4;  // row = head-dim index
+                const uint8_t* g = Vg + int64_t(row) * npad + int64_t(kt) * BC + 16 * (pch ^ TL::vswz(row));
+                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
+            }
+        };
+        constexpr int K_OFF0 = 0, K_OFF1 = TL::KBYTES, V_OFF0 = 2 * TL::KBYTES, V_OFF1 = 2 * TL::KBYTES + TL::VBYTES;
 
-    auto softmax_pv = [&](f32x16 (&s)[2], int kt, const char* vt_lds, f32x16 (&nxt)[2], const char* knext) {
-        const int k_lo = kt * BC;
-        // lane half hh holds keys 32hh .. 32hh+31 of the tile: K block 2kt + hh
-        const int kb = min(2 * kt + hh, nkb - 1);
-        const float ct = c2q * a.ks[int64_t(bh) * nkb + kb];
-        const float sv = a.vs[int64_t(bh) * nvb + kt];
-        const int e8v = (__float_as_uint(sv) >> 23) & 0xFF;  // power of two -> E8M0
-        if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
-            const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 32 * hh;
-#pragma unroll
+        // Q^T operand: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31]
+        i32x8 qreg[KS];
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+            if (qi < a.N) {
+                const uint8_t* p = Qg + int64_t(qi) * D + 64 * ks + 32 * hh;
+                lo = *reinterpret_cast<const uint4*>(p);
+                hi = *reinterpret_cast<const uint4*>(p + 16);
+            }
+            qreg[ks] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        }
+        const float sq = (q0 < a.N) ? a.qs[int64_t(bh) * nqb + q0 / kQBlk] : 1.f;
+        const float c2q = a.scale_log2 * sq;
+
+        f32x16 oacc[DT];
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) oacc[dt][g] = 0.f;
+        float m_ref = -FLT_MAX;  // log2 units of the true scaled score
+        float lsum = 0.f;        // this lane's share of sum(256 p)
+
+        auto scores = [&](f32x16 (&s)[2], const char* kt_lds) {
+    #pragma unroll
+            for (int st = 0; st < 2; ++st) {
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
+                const int row = krow8(j, st);
+                const char* rp = kt_lds + row * D;
+                const int sw = TL::kswz(row);
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh) ^ sw));
+                    const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh + 1) ^ sw));
+                    const i32x8 ka = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+                    s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qreg[ks], s[st], 0, 0, 0, 127, 0, 127);
+                }
+            }
+        };
+
+        auto softmax_pv = [&](f32x16 (&s)[2], int kt, const char* vt_lds, f32x16 (&nxt)[2], const char* knext) {
+            const int k_lo = kt * BC;
+            // lane half hh holds keys 32hh .. 32hh+31 of the tile: K block 2kt + hh
+            const int kb = min(2 * kt + hh, nkb - 1);
+            const float ct = c2q * a.ks[int64_t(bh) * nkb + kb];
+            const float sv = a.vs[int64_t(bh) * nvb + kt];
+            const int e8v = (__float_as_uint(sv) >> 23) & 0xFF;  // power of two -> E8M0
+            if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
+                const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 32 * hh;
+    #pragma unroll
+                for (int st = 0; st < 2; ++st)
+    #pragma unroll
+                    for (int g = 0; g < 16; ++g)
+                        if (16 * st + g > lim) s[st][g] = -INFINITY;
+            }
+            float mx = -INFINITY;
+    #pragma unroll
             for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int g = 0; g < 16; ++g)
-                    if (16 * st + g > lim) s[st][g] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int g = 0; g < 16; ++g) mx = fmaxf(mx, s[st][g]);
-        const float mt = pair_max8(mx * ct);
-        if (__any(mt > m_ref + a.tau)) {
-            const float mn = fmaxf(m_ref, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
-            lsum *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
-            m_ref = mn;
-        }
-        scores(nxt, knext);
-        const float bias = 8.f - m_ref;  // exp2(s*ct - m + 8) = 256 p
-        i32x8 pb;
-        float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 0], ct, bias));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 1], ct, bias));
-                const float p2 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 2], ct, bias));
-                const float p3 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 3], ct, bias));
-                ls0 += p0 + p1;
-                ls1 += p2 + p3;
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                pb[4 * st + r] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) mx = fmaxf(mx, s[st][g]);
+            const float mt = pair_max8(mx * ct);
+            if (__any(mt > m_ref + a.tau)) {
+                const float mn = fmaxf(m_ref, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+                lsum *= alpha;
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                    for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
+                m_ref = mn;
             }
-        lsum += ls0 + ls1;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int row = 32 * dt + j;
-            const char* rp = vt_lds + row * BC;
-            const int sw = TL::vswz(row);
-            const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh) ^ sw));
-            const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh + 1) ^ sw));
-            const i32x8 va = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[dt], 0, 0, 0, e8v, 0, 127);
+            scores(nxt, knext);
+            const float bias = 8.f - m_ref;  // exp2(s*ct - m + 8) = 256 p
+            i32x8 pb;
+            float ls0 = 0.f, ls1 = 0.f;
+    #pragma unroll
+            for (int st = 0; st < 2; ++st)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 0], ct, bias));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 1], ct, bias));
+                    const float p2 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 2], ct, bias));
+                    const float p3 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 3], ct, bias));
+                    ls0 += p0 + p1;
+                    ls1 += p2 + p3;
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    pb[4 * st + r] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+                }
+            lsum += ls0 + ls1;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int row = 32 * dt + j;
+                const char* rp = vt_lds + row * BC;
+                const int sw = TL::vswz(row);
+                const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh) ^ sw));
+                const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh + 1) ^ sw));
+                const i32x8 va = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+                oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[dt], 0, 0, 0, e8v, 0, 127);
+            }
+        };
+
+        if (nt > 0) {
+            copy_k(0, K_OFF0);
+            copy_v(0, V_OFF0);
         }
-    };
-
-    if (nt > 0) {
-        copy_k(0, K_OFF0);
-        copy_v(0, V_OFF0);
-    }
-    if (nt > 1) copy_k(1, K_OFF1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 sA[2], sB[2];
-    if (wnt > 0) scores(sA, smem + K_OFF0);
-    __syncthreads();
-
-    auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
-                    int v_cur_off, int v_nxt_off) {
-        if (kt + 2 < nt) copy_k(kt + 2, k_cur_off);
-        if (kt + 1 < nt) copy_v(kt + 1, v_nxt_off);
-        if (kt < wnt) softmax_pv(cur, kt, smem + v_cur_off, nxt, smem + k_nxt_off);
+        if (nt > 1) copy_k(1, K_OFF1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    };
-    for (int kt = 0; kt < nt; kt += 2) {
-        step(kt, sA, sB, K_OFF0, K_OFF1, V_OFF0, V_OFF1);
-        if (kt + 1 < nt) step(kt + 1, sB, sA, K_OFF1, K_OFF0, V_OFF1, V_OFF0);
-    }
+        f32x16 sA[2], sB[2];
+        if (wnt > 0) scores(sA, smem + K_OFF0);
+        __syncthreads();
 
-    if (qi < a.N && wnt > 0) {
-        const float lt = pair_sum8(lsum);
-        const float inv = 1.0f / lt;
-        uint16_t* orow = Og + int64_t(qi) * a.oss;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                __bf16 o4[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * r + t] * inv);
-                *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, o4);
-            }
-        if (hh == 0)
-            a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt) - 8.f) * 0.69314718055994531f;
+        auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
+                        int v_cur_off, int v_nxt_off) {
+            if (kt + 2 < nt) copy_k(kt + 2, k_cur_off);
+            if (kt + 1 < nt) copy_v(kt + 1, v_nxt_off);
+            if (kt < wnt) softmax_pv(cur, kt, smem + v_cur_off, nxt, smem + k_nxt_off);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        for (int kt = 0; kt < nt; kt += 2) {
+            step(kt, sA, sB, K_OFF0, K_OFF1, V_OFF0, V_OFF1);
+            if (kt + 1 < nt) step(kt + 1, sB, sA, K_OFF1, K_OFF0, V_OFF1, V_OFF0);
+        }
+
+        if (qi < a.N && wnt > 0) {
+            const float lt = pair_sum8(lsum);
+            const float inv = 1.0f / lt;
+            uint16_t* orow = Og + int64_t(qi) * a.oss;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    __bf16 o4[4];
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * r + t] * inv);
+                    *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, o4);
+                }
+            if (hh == 0)
+                a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt) - 8.f) * 0.69314718055994531f;
+        }
     }
 }
 
@@ -434,7 +442,7 @@ int launch_a(const Fp8Args& a, hipStream_t s) {
         attr_set = true;
     }
     const int n_qt = (a.N + NW * WQ - 1) / (NW * WQ);
-    const int64_t grid = int64_t(n_qt) * a.B * a.H;
+    const int64_t grid = int64_t(CAUSAL ? (n_qt + 1) / 2 : n_qt) * a.B * a.H;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), LDS, s, a);
     return static_cast<int>(hipGetLastError());
 }
