@@ -279,6 +279,14 @@ def bench_merge(args, w, dev):
                      "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w),
                      "kernel_ms": round(ms_ev, 5)},
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         import oracle
         S, B, H, N, d = o_parts.shape
