@@ -8,7 +8,10 @@
 // (sec. 8.1).  Queries are split across waves, K/V are shared (sec. 8.3).
 // The maximum the exponentials refer to only advances when a tile's maximum
 // exceeds it by more than tau ("FlashAttention-4" explainer, 論文 Section 3.3);
-// the output stays exact by the rescaling identity (sec. 6.3).  The score
+// the output stays exact by the rescaling identity (sec. 6.3).  The kernel
+// does not take every tile's row maximum first: it forms the probabilities
+// against the current reference and uses their partial row sums, which bound
+// every probability, to detect the rare tile that needs the maximum.  The score
 // product of the next tile is issued before the softmax of the current one so
 // that matrix-core and vector work overlap (the two-stage GEMM/softmax
 // pipelining of the FlashAttention-3 note, section 技術 2).
@@ -252,45 +255,64 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         return pair_max(mx);
     };
 
-    // The reference maximum advances only when the tile maximum exceeds it by
-    // more than tau; the decision is wave-uniform (rescaling is always exact).
-    auto advance_max = [&](float mx) {
-        const float mt = mx * c2;
-        if (__any(mt > m_ref + a.tau)) {
-            const float mn = fmaxf(m_ref, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
-            lsum *= alpha;
+    // ---- softmax with a speculative reference maximum ------------------------
+    // A tile's probabilities are formed with the reference maximum m_ref as it
+    // stands, without a pass over the tile's own row maximum.  Every p is
+    // non-negative, so a lane's partial row sum bounds each p it holds: while
+    // no partial sum exceeds 2^tau, no score exceeds m_ref + tau and the
+    // reference may stay (the threshold rule of the "FlashAttention-4"
+    // explainer, 論文 Section 3.3).  Otherwise, before any of the tile's
+    // probabilities reach O, a slow path takes the tile's true row maximum,
+    // applies the same rule (rescale when the maximum exceeds m_ref by more
+    // than tau; exact per-lane rescaling of O and l, sec. 6.3) and recomputes
+    // the tile's probabilities.  The rescale decisions are those of the
+    // max-first formulation.
+    const float thr = exp2f(a.tau);
+    auto rescale = [&](const f32x16 (&s)[2]) -> bool {
+        const float mt = tile_max(s) * c2;
+        if (!__any(mt > m_ref + a.tau)) return false;
+        const float mn = fmaxf(m_ref, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+        lsum *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
-            m_ref = mn;
-        }
+            for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
+        m_ref = mn;
+        return true;
+    };
+    // probabilities of score pair p (0..15: chunk p / 4, elements 2*(p % 4), +1)
+    auto exp_pair = [&](const f32x16 (&s)[2], int p, bf16x8 (&pb)[4], float& acc) {
+        const float neg_m = -m_ref;
+        const int c = p >> 2, e = 2 * (p & 3);
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + e], c2, neg_m));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + e + 1], c2, neg_m));
+        const bf16x2 pr = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+        pb[c][e] = pr[0];
+        pb[c][e + 1] = pr[1];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, acc, false);
     };
 
     // One straight-line block per tile, issued in fenced chunks so that every
     // matrix-core instruction has independent vector work beside it:
     //  phase 1: score MFMAs of the next tile (K operands read NPK MFMAs ahead),
     //           each paired with probabilities of the current tile
-    //           (fma, exp2, bf16 pack, row-sum dot2);
-    //  phase 2: PV MFMAs of the current tile (V^T operands read NPV ahead),
-    //           each paired with part of the next tile's row maximum (a tile
-    //           that needs a mask gets it, and its maximum, afterwards).
+    //           (fma, exp2, bf16 pack, row-sum dot2); then the check above;
+    //  phase 2: PV MFMAs of the current tile (V^T operands read NPV ahead).
     // On a wave's last tile the score product reads a valid but unused buffer.
     constexpr int QKM = 2 * KSTEPS;   // score MFMAs per tile
     constexpr int PVM = 4 * DT;       // PV MFMAs per tile
     constexpr int NPAIR = 16;         // probability pairs per lane per tile
     constexpr int PPM = NPAIR / QKM;  // pairs per score MFMA
     constexpr int NPK = 2, NPV = 2;
-    static_assert(NPAIR % QKM == 0 && 16 % PVM == 0, "phase split");
-    auto main_block = [&](f32x16 (&s)[2], const char* vt_lds, f32x16 (&nxt)[2], const char* knext) -> float {
-        const float neg_m = -m_ref;
+    static_assert(NPAIR % QKM == 0, "phase split");
+    auto main_block = [&](f32x16 (&s)[2], const char* vt_lds, f32x16 (&nxt)[2], const char* knext) {
         bf16x8 pb[4];
         bf16x8 kb[NPK];
 #pragma unroll
         for (int i = 0; i < NPK; ++i) kb[i] = k_operand(knext, i);
-        const f32x16 zero = {};
         float lpart[2] = {0.f, 0.f};  // two independent row-sum chains
+        const f32x16 zero = {};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < QKM; ++m) {
@@ -299,37 +321,30 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
             nxt[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[m >> 1], (m < 2) ? zero : nxt[m & 1], 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < PPM; ++q) {
-                const int p = m * PPM + q;          // pair p: chunk p / 4, elements 2*(p % 4), +1
-                const int c = p >> 2, e = 2 * (p & 3);
-                const float x0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + e], c2, neg_m));
-                const float x1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + e + 1], c2, neg_m));
-                const bf16x2 pr = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-                pb[c][e] = pr[0];
-                pb[c][e + 1] = pr[1];
-                lpart[p & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lpart[p & 1], false);
+                const int p = m * PPM + q;
+                exp_pair(s, p, pb, lpart[p & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        lsum += lpart[0] + lpart[1];
+        float lp = lpart[0] + lpart[1];
+        if (__any(lp > thr) && rescale(s)) {
+            lpart[0] = lpart[1] = 0.f;
+#pragma unroll
+            for (int p = 0; p < NPAIR; ++p) exp_pair(s, p, pb, lpart[p & 1]);
+            lp = lpart[0] + lpart[1];
+        }
+        lsum += lp;
         bf16x8 vb[NPV];
 #pragma unroll
         for (int i = 0; i < NPV; ++i) vb[i] = v_operand(vt_lds, i);
-        float mxp[2] = {-INFINITY, -INFINITY};  // two independent max chains
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < PVM; ++n) {
             const bf16x8 va = vb[n % NPV];
             if (n + NPV < PVM) vb[n % NPV] = v_operand(vt_lds, n + NPV);
             oacc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n / DT], oacc[n % DT], 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 16 / PVM; ++q) {    // two score registers per step
-                const int r = 2 * (n * (16 / PVM) + q);
-                const int ch = (n * (16 / PVM) + q) & 1;
-                mxp[ch] = fmaxf(fmaxf(mxp[ch], nxt[r >> 4][r & 15]), nxt[r >> 4][(r & 15) + 1]);
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        return pair_max(fmaxf(mxp[0], mxp[1]));
     };
 
     // ---- prologue: K0, V0, K1 in flight; S(0) ---------------------------------
@@ -342,11 +357,10 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     __syncthreads();
 
     f32x16 sA[2], sB[2];
-    float mx_cur = -INFINITY;
     if (wnt > 0) {
         scores(sA, smem + K_OFF0);
         if (needs_mask(0)) apply_mask(sA, 0);
-        mx_cur = tile_max(sA);
+        m_ref = tile_max(sA) * c2;  // finite: key 0 is allowed for every query
     }
     __syncthreads();  // every wave is done with K0 before K2 overwrites it
 
@@ -356,12 +370,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         if (kt + 2 < nt) copy_tile(kp, kt + 2, k_cur_off);
         if (kt + 1 < nt) copy_tile(vp, kt + 1, v_nxt_off);
         if (kt < wnt) {
-            advance_max(mx_cur);
-            mx_cur = main_block(cur, smem + v_cur_off, nxt, smem + k_nxt_off);
-            if (needs_mask(kt + 1)) {  // at most the diagonal and the ragged tile
-                apply_mask(nxt, kt + 1);
-                mx_cur = tile_max(nxt);
-            }
+            main_block(cur, smem + v_cur_off, nxt, smem + k_nxt_off);
+            if (needs_mask(kt + 1)) apply_mask(nxt, kt + 1);  // at most the diagonal and the ragged tile
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();

@@ -96,6 +96,28 @@ def test_bf16_tau_agree(tau):
     _check(o, lse, ref, True, "bf16", scale=scale)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mag", [40.0, 400.0])
+def test_bf16_late_dominant_key(causal, mag):
+    """Key 777 of 1000 aligns with every query (a shared component of 6 on
+    head dim 0), so its score jumps far above everything before it: by ~25
+    (log2) with mag 40, which must trigger a rescale, and by ~300 with mag
+    400, where exp2 relative to the earlier maximum would leave the fp32
+    range."""
+    torch = _torch()
+    B, H, N, d = 1, 2, 1000, 128
+    q, k, v = normal_qkv(B, H, N, d, 82)
+    q[..., 0] += 6.0
+    k[:, :, 777, :] = 0.0
+    k[:, :, 777, 0] = mag
+    tens, ref = zip(*(to_bf16(x) for x in (q, k, v)))
+    o, lse = _run([t.cuda() for t in tens], causal)
+    _check(o, lse, ref, causal, "bf16")
+    if mag == 400.0:  # rows that see key 777 return (almost exactly) V[777]
+        first = 777 if causal else 0
+        assert np.max(np.abs(o[0, 0, first:] - ref[2][0, 0, 777])) <= 2e-2
+
+
 def test_bf16_bnhd_layout():
     """[B, N, H, d] memory viewed as [B, H, N, d] through strides."""
     torch = _torch()
