@@ -193,7 +193,7 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
     a.N = static_cast<int32_t>(o_layout.seqlen);
     a.D = static_cast<int32_t>(o_layout.head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.tau = fminf(tau, 0.5f);  // 256 * 2^tau must stay below 448
+    a.tau = fminf(tau, 2.5f);  // 64 * 2^tau must stay below 448
     a.causal = causal;
     a.tile_cfg = tile_cfg;
     return hip_status(fa::launch_fwd_fp8(a, stream));

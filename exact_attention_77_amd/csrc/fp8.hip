@@ -26,8 +26,9 @@
 //    Q and K block scales fold into the exp2 constant (the Q block is the
 //    wave's 32 rows, the K block the 32 keys a lane half holds, so both are
 //    per-lane scalars); the V block scale is a power of two handed to the
-//    matrix core as its E8M0 A-operand scale.  Probabilities enter as e4m3(256 p); the row sum and O carry the
-//    same factor 256, which cancels in O / l and is removed from the LSE.
+//    matrix core as its E8M0 A-operand scale.  Probabilities enter as e4m3(64 p) with p <= 2^tau (tau capped at
+//    2.5, so 64 p stays below e4m3's 448); the row sum and O carry the same factor 64, which cancels in O / l
+//    and is removed from the LSE.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <math.h>
@@ -297,7 +298,7 @@ void fwd_fp8_kernel(Fp8Args a) {
     #pragma unroll
             for (int g = 0; g < 16; ++g) oacc[dt][g] = 0.f;
         float m_ref = -FLT_MAX;  // log2 units of the true scaled score
-        float lsum = 0.f;        // this lane's share of sum(256 p)
+        float lsum = 0.f;        // this lane's share of sum(64 p)
 
         auto scores = [&](f32x16 (&s)[2], const char* kt_lds) {
     #pragma unroll
@@ -349,7 +350,7 @@ void fwd_fp8_kernel(Fp8Args a) {
                 m_ref = mn;
             }
             scores(nxt, knext);
-            const float bias = 8.f - m_ref;  // exp2(s*ct - m + 8) = 256 p
+            const float bias = 6.f - m_ref;  // exp2(s*ct - m + 6) = 64 p
             i32x8 pb;
             float ls0 = 0.f, ls1 = 0.f;
     #pragma unroll
@@ -416,7 +417,7 @@ void fwd_fp8_kernel(Fp8Args a) {
                     *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, o4);
                 }
             if (hh == 0)
-                a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt) - 8.f) * 0.69314718055994531f;
+                a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt) - 6.f) * 0.69314718055994531f;
         }
     }
 }

@@ -148,7 +148,7 @@ int64_t flash_attn_fp8_num_scales(flash_attn_layout layout, flash_attn_fp8_role 
  * the matrix products run on the fp8 matrix cores with fp32 accumulation.  Q/K
  * block scales fold into the softmax exponent, the power-of-two V scales are
  * applied by the matrix cores, and the probabilities enter the second product
- * as e4m3(256 p) (p <= 2^0.5: tau is capped at 0.5 here); the row sum uses the
+ * as e4m3(64 p) (p <= 2^2.5: tau is capped at 2.5 here); the row sum uses the
  * fp32 p.  O is bf16 with the strides of `o_layout`, whose batch, heads,
  * seqlen and head_dim give the shape of everything; LSE is fp32 [B, H, N].
  */
