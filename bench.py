@@ -58,7 +58,7 @@ def measured_traffic(w):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))[w.name]
-        if any(fingerprint(src) != fp for src, fp in rec["fingerprints"].items()):
+        if any(fingerprint(os.path.basename(src)) != fp for src, fp in rec["fingerprints"].items()):
             return None
     except (OSError, KeyError, ValueError, AttributeError):
         return None

@@ -1,0 +1,38 @@
+"""Host-side logic of bench.py (no GPU): the HBM-traffic record lookup."""
+import json
+import os
+
+import pytest
+
+import bench
+from exact_attention_77_amd.build import fingerprint
+from synth_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+RECORD = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def _records():
+    return {k: v for k, v in json.load(open(RECORD)).items() if isinstance(v, dict)}
+
+
+@pytest.mark.parametrize("name", sorted(_records()))
+def test_traffic_record_is_found_when_sources_match(name):
+    rec = _records()[name]
+    current = all(fingerprint(os.path.basename(s)) == f for s, f in rec["fingerprints"].items())
+    got = bench.measured_traffic(WORKLOADS[name])
+    if current:
+        assert got == rec["read_bytes"] + rec["write_bytes"] and got > 0
+    else:
+        assert got is None
+
+
+def test_traffic_record_rejected_after_source_change(tmp_path, monkeypatch):
+    name = sorted(_records())[0]
+    recs = json.load(open(RECORD))
+    src = next(iter(recs[name]["fingerprints"]))
+    recs[name]["fingerprints"][src] = "0" * 16          # as if the kernel had changed
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "hbm_traffic.json").write_text(json.dumps(recs))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic(WORKLOADS[name]) is None
