@@ -65,6 +65,42 @@ def measured_traffic(w):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+def launch_stats(step, stream, dev, n):
+    """After the timed region: n launches with one HIP event pair each (median
+    and minimum), then three cold launches, each after a 512 MiB scrub write
+    that evicts the inputs from L2 and the 256 MB last-level cache."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    lat = sorted(a.elapsed_time(b) for a, b in ev)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(3):
+        scrub.fill_(i + 1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del scrub
+    return {"launches": n, "median_ms": round(lat[n // 2], 5), "min_ms": round(lat[0], 5),
+            "cold_ms": round(sorted(cold)[1], 5), "cold_scrub_bytes": 512 << 20}
+
+
+def device_info():
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name or torch.cuda.get_device_name(0) or None, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "hip": torch.version.hip}
+
+
 def cpu_baseline(w, target_s):
     """Time the fp64 oracle on a bounded, seeded sample of the workload: whole
     (batch, head) slices in a seeded order until about target_s of wall time."""
@@ -200,6 +236,7 @@ def main():
     tflops = w.flops / (ms * 1e-3) / 1e12
     kernel_tflops = w.flops / (ms_ev * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    timing = launch_stats(step, stream, dev, min(50, args.steps))
 
     out = {
         "metric": METRIC if w.name == "bf16_causal_n8192_d128" else
@@ -223,6 +260,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": measured_traffic(w), "kernel_ms": round(ms_ev, 5)},
+        "timing": timing,
+        "device": device_info(),
     }
     out.update(extra)
     if args.copy_calibration_mib:
@@ -268,6 +307,7 @@ def bench_merge(args, w, dev):
     ms = max(ms_ev, (time.perf_counter() - t0) * 1e3 / args.steps)
     gbs = w.merge_bytes / (ms * 1e-3) / 1e9
     kgbs = w.merge_bytes / (ms_ev * 1e-3) / 1e9
+    timing = launch_stats(step, stream, dev, min(50, args.steps))
     out = {
         "metric": f"attention merge GB/s ({w.name})", "value": round(gbs, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -278,6 +318,8 @@ def bench_merge(args, w, dev):
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w),
                      "kernel_ms": round(ms_ev, 5)},
+        "timing": timing,
+        "device": device_info(),
     }
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
