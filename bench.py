@@ -97,8 +97,12 @@ def device_info():
     import torch
 
     p = torch.cuda.get_device_properties(0)
-    return {"name": p.name or torch.cuda.get_device_name(0) or None, "arch": getattr(p, "gcnArchName", None),
-            "compute_units": p.multi_processor_count, "hip": torch.version.hip}
+    info = {"arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hip": torch.version.hip}
+    name = p.name or torch.cuda.get_device_name(0)
+    if name:  # empty where the marketing-name table is not installed
+        info["name"] = name
+    return info
 
 
 def cpu_baseline(w, target_s):

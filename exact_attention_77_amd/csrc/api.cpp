@@ -63,7 +63,7 @@ flash_attn_status check_opts(const flash_attn_fwd_opts* opts, float* tau, int* t
         if (!(opts->tau_log2 <= 64.0f)) return FLASH_ATTN_ERR_ARG;
         *tau = opts->tau_log2;
     }
-    if (opts->tile_cfg < 0 || opts->tile_cfg > 3) return FLASH_ATTN_ERR_ARG;
+    if (opts->tile_cfg < 0 || opts->tile_cfg > 2) return FLASH_ATTN_ERR_ARG;
     *tile_cfg = opts->tile_cfg;
     return FLASH_ATTN_OK;
 }

@@ -76,8 +76,10 @@ typedef struct flash_attn_layout {
  *   on tau (the rescaling identity, FlashAttention page sec. 6.3) beyond fp32
  *   rounding; unnormalised probabilities stay below 2^tau.  Range [0, 64];
  *   a negative value selects the default 8.
- * tile_cfg: 0 = automatic; other values select an alternative kernel
- *   configuration (used by tests to cross-check configurations). */
+ * tile_cfg: 0 = automatic (bf16: 4-wave workgroups of 128 query rows for
+ *   head_dim 64, 8-wave workgroups of 256 rows for 128); 1 and 2 force the
+ *   8- and 4-wave forms of the bf16 kernel; any other value is an argument
+ *   error.  The result does not depend on it beyond fp32 summation order. */
 typedef struct flash_attn_fwd_opts {
     float tau_log2;
     int32_t tile_cfg;

@@ -105,7 +105,8 @@ def test_bad_causal_flag():
 
 
 @pytest.mark.parametrize("opts", [fa.FwdOpts(65.0, 0, 0), fa.FwdOpts(float("nan"), 0, 0),
-                                  fa.FwdOpts(8.0, 9, 0), fa.FwdOpts(8.0, 0, 1)])
+                                  fa.FwdOpts(8.0, 9, 0), fa.FwdOpts(8.0, 3, 0), fa.FwdOpts(8.0, -1, 0),
+                                  fa.FwdOpts(8.0, 0, 1)])
 def test_bad_options(opts):
     assert fwd(opts=ctypes.byref(opts)) == 6
 

@@ -79,10 +79,12 @@ def test_parity_full_compare(dtype, causal, d, N):
     _check(o, lse, ref, causal, dtype)
 
 
-@pytest.mark.parametrize("tile_cfg", [0, 2])
+@pytest.mark.parametrize("tile_cfg", [0, 1, 2])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bf16_tile_configs(tile_cfg, causal):
-    dev, ref = _inputs(1, 4, 1000, 128, 77, "bf16")
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_tile_configs(tile_cfg, causal, d):
+    """Every workgroup shape (automatic, 8 waves, 4 waves) on a ragged N."""
+    dev, ref = _inputs(1, 4, 1000, d, 77, "bf16")
     o, lse = _run(dev, causal, tile_cfg=tile_cfg)
     _check(o, lse, ref, causal, "bf16")
 
