@@ -35,11 +35,41 @@ PER_FILE = {
 }
 
 
+def strip_comments(text: str) -> str:
+    """C/C++ source without its comments (string and character literals are
+    kept intact; a comment becomes one space, and line structure is kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                       # literal: copy through its end
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" " + "\n" * text.count("\n", i, n if j < 0 else j))
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def fingerprint(src: str) -> str:
-    """sha256 prefix of a csrc/ source file plus the flags it is compiled with:
-    it changes whenever the kernel binary built from that file can change."""
+    """sha256 prefix of a csrc/ source file (comments, blank lines and the
+    indentation removed) plus the flags it is compiled with: it changes
+    whenever the kernel binary built from that file can change, and not for
+    an edit of its comments or layout alone."""
     import hashlib
-    h = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read())
+    text = open(os.path.join(CSRC, src), encoding="utf-8").read()
+    lines = (ln.strip() for ln in strip_comments(text).splitlines())
+    h = hashlib.sha256("\n".join(ln for ln in lines if ln).encode())
     h.update(repr((COMMON, PER_FILE.get(src, []), ARCH)).encode())
     return h.hexdigest()[:16]
 

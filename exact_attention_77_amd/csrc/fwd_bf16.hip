@@ -266,7 +266,9 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     // applies the same rule (rescale when the maximum exceeds m_ref by more
     // than tau; exact per-lane rescaling of O and l, sec. 6.3) and recomputes
     // the tile's probabilities.  The rescale decisions are those of the
-    // max-first formulation.
+    // max-first formulation (up to the bf16 rounding of a p lying within one
+    // bf16 step of 2^tau, where either choice is exact).  An overflowing
+    // exp2 gives an infinite sum and so also takes the slow path.
     const float thr = exp2f(a.tau);
     auto rescale = [&](const f32x16 (&s)[2]) -> bool {
         const float mt = tile_max(s) * c2;

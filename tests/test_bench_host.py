@@ -36,3 +36,25 @@ def test_traffic_record_rejected_after_source_change(tmp_path, monkeypatch):
     (tmp_path / "profiles" / "hbm_traffic.json").write_text(json.dumps(recs))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic(WORKLOADS[name]) is None
+
+
+def test_strip_comments_keeps_code_and_literals():
+    from exact_attention_77_amd.build import strip_comments
+    src = ('int a = 1; // one\n'
+           'const char* s = "// kept /* kept */";\n'
+           '/* two\n   lines */ char q = \'\\\'\'; char r = \'"\';\n')
+    out = strip_comments(src)
+    assert "one" not in out and "two" not in out and "lines" not in out
+    assert '"// kept /* kept */"' in out and "char q = '\\''" in out and "char r = '\"'" in out
+    assert out.count("\n") == src.count("\n")
+
+
+def test_fingerprint_ignores_comment_edits_only(tmp_path, monkeypatch):
+    from exact_attention_77_amd import build
+    (tmp_path / "k.hip").write_text("__global__ void k(int* p) { p[0] = 1; }  // a kernel\n")
+    monkeypatch.setattr(build, "CSRC", str(tmp_path))
+    f0 = build.fingerprint("k.hip")
+    (tmp_path / "k.hip").write_text("/* the same kernel */\n__global__ void k(int* p) { p[0] = 1; }\n")
+    assert build.fingerprint("k.hip") == f0
+    (tmp_path / "k.hip").write_text("__global__ void k(int* p) { p[0] = 2; }\n")
+    assert build.fingerprint("k.hip") != f0
