@@ -190,3 +190,16 @@ def test_merge_validation():
     assert merge(lay=_lay(d=96)) == 5
     assert merge(o=P + 8) == 3
     assert merge(o_parts=None, lse_parts=None, o=None, lse=None, lay=_lay(N=0)) == 0
+
+
+def test_c_consumer_compiles(tmp_path):
+    """The C consumer builds against the public header and the two libraries."""
+    import importlib.util
+    import subprocess
+    spec = importlib.util.spec_from_file_location("c_api_build", os.path.join(
+        os.path.dirname(os.path.abspath(__file__)), "c_api", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = str(tmp_path / "abi_consumer")
+    subprocess.run(mod.command(out), check=True)
+    assert os.path.getsize(out) > 0

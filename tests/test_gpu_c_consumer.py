@@ -1,0 +1,20 @@
+"""The library used from C alone: tests/c_api/abi_consumer (built by the
+package build) runs one causal bf16 forward through include/flash_attn.h on
+HIP device buffers, checks it against the fp64 oracle (max |dO| <= 2e-2,
+max |dLSE| <= 1e-2) and two synchronous error returns."""
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_api", "abi_consumer")
+
+
+def test_c_consumer_runs():
+    if not os.path.exists(EXE):
+        pytest.fail("tests/c_api/abi_consumer is not built (run __graft_entry__.build())")
+    r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK")
