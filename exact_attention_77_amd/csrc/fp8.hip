@@ -60,114 +60,146 @@ __device__ __forceinline__ int cvt2(float a, float b, int old) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
+// One workgroup (4 waves) takes RWG consecutive rows of one (b, h); a lane
+// holds 32 consecutive elements of one row (LPR = D / 32 lanes per row), so a
+// row's Walsh-Hadamard transform is five butterfly stages inside the lane and
+// log2(LPR) stages across neighbouring lanes (DPP quad permutes, no LDS).
+// A scale block (32 or 64 rows) is one or more whole waves.
 template <int D, bool IN_BF16>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantArgs a) {
-    constexpr int LPR = D / 4;     // lanes per row
-    constexpr int RPW = 64 / LPR;  // rows per wave per pass
-    constexpr int RPP = 4 * RPW;   // rows per workgroup pass
-    constexpr int MAXP = kVBlk / RPP;  // the largest block
+    constexpr int LPR = D / 32;       // lanes per row
+    constexpr int RPW = 64 / LPR;     // rows per wave
+    constexpr int RWG = 4 * RPW;      // rows per workgroup
+    static_assert(RPW % kQBlk == 0 || kQBlk % RPW == 0, "scale block / wave mismatch");
     __shared__ float red[4];
-    __shared__ __attribute__((aligned(16))) uint8_t vt_tile[D * kVBlk];
+    // V^T staging: D rows of RWG key bytes; the keys of head-dim chunk c are
+    // rotated by 16c bytes so that the byte writes of one instruction spread
+    // over the banks (16-byte groups stay contiguous for the row reads).
+    __shared__ __attribute__((aligned(16))) uint8_t vt_tile[D * RWG];
 
     const int blk_rows = (a.role == 0) ? kQBlk : (a.role == 1) ? kKBlk : kVBlk;
-    const int npass = blk_rows / RPP;
     const int nblk = (a.N + blk_rows - 1) / blk_rows;
-    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int nwg = (a.N + RWG - 1) / RWG;
+    const int bh = blockIdx.x / nwg, g = blockIdx.x % nwg;
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = 4 * (lane % LPR);
-    const int rsub = lane / LPR;
-    const int64_t xbase = int64_t(b) * a.sb + int64_t(h) * a.sh;
+    const int c = lane % LPR;                    // columns 32c .. 32c+31
+    const int rw = wave * RPW + lane / LPR;      // row inside the workgroup
+    const int row = g * RWG + rw;
+    const int64_t xoff = int64_t(b) * a.sb + int64_t(h) * a.sh + int64_t(row) * a.ss + 32 * c;
 
-    float sg[4] = {1.f, 1.f, 1.f, 1.f};
-    if (a.rotate)
+    float x[32];
+    if (row < a.N) {
+        if (IN_BF16) {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + xoff);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sg[e] = static_cast<float>(a.signs[col + e]);
-    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
-
-    float v[MAXP][4];
-    float amax = 0.f;
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        const int row = blk * blk_rows + p * RPP + wave * RPW + rsub;
-        if (p < npass && row < a.N) {
-            const int64_t off = xbase + int64_t(row) * a.ss + col;
-            if (IN_BF16) {
-                const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.x) + off);
-                x[0] = __uint_as_float(r.x << 16); x[1] = __uint_as_float(r.x & 0xFFFF0000u);
-                x[2] = __uint_as_float(r.y << 16); x[3] = __uint_as_float(r.y & 0xFFFF0000u);
-            } else {
-                const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + off);
-                x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
-            }
-        }
-        if (a.rotate) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] *= sg[e];
-            // Walsh-Hadamard butterflies: element index 4*(lane % LPR) + e.
-            float y0 = x[0] + x[1], y1 = x[0] - x[1], y2 = x[2] + x[3], y3 = x[2] - x[3];
-            x[0] = y0 + y2; x[1] = y1 + y3; x[2] = y0 - y2; x[3] = y1 - y3;
-#pragma unroll
-            for (int m = 1; m < LPR; m <<= 1) {
-                const bool upper = (lane & m) != 0;
+            for (int i = 0; i < 4; ++i) {
+                const uint4 r = p[i];
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float o = __shfl_xor(x[e], m, 64);
-                    x[e] = upper ? (o - x[e]) : (x[e] + o);
+                    x[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+                    x[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
                 }
             }
+        } else {
+            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + xoff);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] *= inv_sqrt_d;
+            for (int i = 0; i < 8; ++i) {
+                const float4 r = p[i];
+                x[4 * i] = r.x; x[4 * i + 1] = r.y; x[4 * i + 2] = r.z; x[4 * i + 3] = r.w;
+            }
         }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[p][e] = x[e];
-            amax = fmaxf(amax, fabsf(x[e]));
-        }
+        for (int i = 0; i < 32; ++i) x[i] = 0.f;
     }
+
+    if (a.rotate) {
+        // signs of columns 32c .. 32c+31 (byte loads: the vector may have any alignment)
+        const int8_t* sp = a.signs + 32 * c;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (sp[i] < 0) x[i] = -x[i];
+        // butterflies on index bits 0-4 (inside the lane): (u, v) -> (u + v, u - v)
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1)
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                if (!(i & m)) {
+                    const float u = x[i], v = x[i + m];
+                    x[i] = u + v;
+                    x[i + m] = u - v;
+                }
+        // index bits 5 and 6: the partner row chunk is lane ^ 1 (and lane ^ 2)
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) {
+            const bool upper = (lane & m) != 0;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const int xi = __float_as_int(x[i]);
+                const int o = (m == 1) ? __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false)    // quad_perm 1,0,3,2
+                                       : __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+                x[i] = upper ? (__int_as_float(o) - x[i]) : (x[i] + __int_as_float(o));
+            }
+        }
+        const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] *= inv_sqrt_d;
+    }
+
+    // absolute maximum of each scale block: lane, wave, then the block's waves
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
     if (lane == 0) red[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int wpb = blk_rows >= RPW ? blk_rows / RPW : 1;   // waves per scale block
+    const int w0 = (wave / wpb) * wpb;
+    amax = red[w0];
+    for (int w = w0 + 1; w < w0 + wpb; ++w) amax = fmaxf(amax, red[w]);
     float scale = (amax > 0.f) ? amax / 448.f : 1.f;
     if (a.role == 2 && amax > 0.f) {  // power-of-two ceiling for V
         int e;
         const float m = frexpf(scale, &e);
         scale = (m == 0.5f) ? scale : ldexpf(1.f, e);
     }
-    if (tid == 0) a.scales[int64_t(bh) * nblk + blk] = scale;
+    const int blk = row / blk_rows;
+    if (rw % blk_rows == 0 && c == 0 && blk < nblk) a.scales[int64_t(bh) * nblk + blk] = scale;
+    const float rcp = 1.0f / scale;
+
+    uint32_t wq[8];   // e4m3 codes of the lane's 32 elements, 4 per word
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int lo = cvt2<false>(x[4 * i] * rcp, x[4 * i + 1] * rcp, 0);
+        wq[i] = static_cast<uint32_t>(cvt2<true>(x[4 * i + 2] * rcp, x[4 * i + 3] * rcp, lo));
+    }
 
     if (a.role != 2) {
-#pragma unroll
-        for (int p = 0; p < MAXP; ++p) {
-            const int row = blk * blk_rows + p * RPP + wave * RPW + rsub;
-            if (p < npass && row < a.N) {
-                int w = cvt2<false>(v[p][0] / scale, v[p][1] / scale, 0);
-                w = cvt2<true>(v[p][2] / scale, v[p][3] / scale, w);
-                *reinterpret_cast<int*>(a.out + (int64_t(bh) * a.N + row) * D + col) = w;
-            }
+        if (row < a.N) {
+            uint4* op = reinterpret_cast<uint4*>(a.out + (int64_t(bh) * a.N + row) * D + 32 * c);
+            op[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+            op[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
         }
         return;
     }
-    // V: transpose through LDS, [d][64 keys] bytes, rows past N are zero.
+    // V: [D][RWG] bytes through LDS (rows past N hold zero codes), then rows of
+    // V^T written 16 bytes at a time.
+    const int col = (rw + 16 * c) % RWG;
 #pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-        if (p < npass) {
-            const int r = p * RPP + wave * RPW + rsub;  // row inside the block
-            int w = cvt2<false>(v[p][0] / scale, v[p][1] / scale, 0);
-            w = cvt2<true>(v[p][2] / scale, v[p][3] / scale, w);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vt_tile[(col + e) * kVBlk + r] = static_cast<uint8_t>(w >> (8 * e));
-        }
-    }
+    for (int i = 0; i < 32; ++i)
+        vt_tile[(32 * c + i) * RWG + col] = static_cast<uint8_t>(wq[i >> 2] >> (8 * (i & 3)));
     __syncthreads();
     const int64_t npad = fp8_npad(a.N);
-    for (int c = tid; c < D * kVBlk / 16; c += 256) {
-        const int d = c / (kVBlk / 16), part = c % (kVBlk / 16);
-        *reinterpret_cast<uint4*>(a.out + (int64_t(bh) * D + d) * npad + int64_t(blk) * kVBlk + 16 * part) =
-            *reinterpret_cast<const uint4*>(vt_tile + d * kVBlk + 16 * part);
+    constexpr int CPRW = RWG / 16;   // 16-byte chunks per staged row
+    for (int t = tid; t < D * CPRW; t += 256) {
+        const int d = t / CPRW, j = t % CPRW;
+        const int64_t k0 = int64_t(g) * RWG + 16 * j;
+        if (k0 < npad)
+            *reinterpret_cast<uint4*>(a.out + (int64_t(bh) * D + d) * npad + k0) =
+                *reinterpret_cast<const uint4*>(vt_tile + d * RWG + (16 * j + 16 * (d / 32)) % RWG);
     }
 }
 
@@ -424,8 +456,8 @@ void fwd_fp8_kernel(Fp8Args a) {
 
 template <int D, bool BF>
 int launch_q(const QuantArgs& a, hipStream_t s) {
-    const int blk_rows = (a.role == 0) ? kQBlk : (a.role == 1) ? kKBlk : kVBlk;
-    const int64_t grid = int64_t(a.B) * a.H * ((a.N + blk_rows - 1) / blk_rows);
+    constexpr int RWG = 4 * (64 / (D / 32));   // rows per workgroup
+    const int64_t grid = int64_t(a.B) * a.H * ((a.N + RWG - 1) / RWG);
     hipLaunchKernelGGL((fp8_quantize_kernel<D, BF>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
