@@ -214,7 +214,6 @@ template <int D>
 struct Tile8 {
     static constexpr int KBYTES = BC * D;          // K tile [64 keys][D] bytes
     static constexpr int VBYTES = D * BC;          // V^T tile [D][64 keys] bytes
-    static constexpr int LDS_BYTES = 2 * KBYTES + 2 * VBYTES;
     static constexpr int KCPR = D / 16;            // 16-byte chunks per K row
     // K: the 16 rows read together are keys {0..7, 32..39} (+16 st); the
     // swizzle gives each of them its own bank group.
@@ -250,7 +249,13 @@ void fwd_fp8_kernel(Fp8Args a) {
     constexpr int DT = D / 32;   // head-dim tiles of O^T
     constexpr int NBK = TL::KBYTES / 1024, NBV = TL::VBYTES / 1024;
 
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    // Each LDS buffer is its own object and every access names its buffer at
+    // compile time, so the compiler can tell an operand read from a pending
+    // direct-to-LDS copy into another buffer and does not make it wait.
+    __shared__ __attribute__((aligned(1024))) char lds_k0[TL::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[TL::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[TL::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[TL::VBYTES];
 
     // One head per XCD; under the causal mask a workgroup takes the query-tile
     // pair (T-1-p, p), so that all workgroups carry the same work.
@@ -290,24 +295,23 @@ void fwd_fp8_kernel(Fp8Args a) {
         if (q0 >= a.N) wnt = 0;
 
         // direct global -> LDS copies (1 KB per wave instruction, XOR-swizzled rows)
-        auto copy_k = [&](int kt, int off) {
+        auto copy_k = [&](int kt, char* dst) {
             for (int bk = wave; bk < NBK; bk += NW) {
                 const int c = bk * 64 + lane;
                 const int row = c / TL::KCPR, pch = c % TL::KCPR;
                 const int key = min(kt * BC + row, a.N - 1);
                 const uint8_t* g = Kg + int64_t(key) * D + 16 * (pch ^ TL::kswz(row));
-                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(dst + bk * 1024), 16, 0, 0);
             }
         };
-        auto copy_v = [&](int kt, int off) {
+        auto copy_v = [&](int kt, char* dst) {
             for (int bk = wave; bk < NBV; bk += NW) {
                 const int c = bk * 64 + lane;
                 const int row = c / 4, pch = c % 4;  // row = head-dim index
                 const uint8_t* g = Vg + int64_t(row) * npad + int64_t(kt) * BC + 16 * (pch ^ TL::vswz(row));
-                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(smem + off + bk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(dst + bk * 1024), 16, 0, 0);
             }
         };
-        constexpr int K_OFF0 = 0, K_OFF1 = TL::KBYTES, V_OFF0 = 2 * TL::KBYTES, V_OFF1 = 2 * TL::KBYTES + TL::VBYTES;
 
         // Q^T operand: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31]
         i32x8 qreg[KS];
@@ -350,12 +354,12 @@ void fwd_fp8_kernel(Fp8Args a) {
             }
         };
 
-        auto softmax_pv = [&](f32x16 (&s)[2], int kt, const char* vt_lds, f32x16 (&nxt)[2], const char* knext) {
+        auto softmax_pv = [&](f32x16 (&s)[2], int kt, float ksc, float vsc, const char* vt_lds, f32x16 (&nxt)[2],
+                              const char* knext) {
             const int k_lo = kt * BC;
             // lane half hh holds keys 32hh .. 32hh+31 of the tile: K block 2kt + hh
-            const int kb = min(2 * kt + hh, nkb - 1);
-            const float ct = c2q * a.ks[int64_t(bh) * nkb + kb];
-            const float sv = a.vs[int64_t(bh) * nvb + kt];
+            const float ct = c2q * ksc;
+            const float sv = vsc;
             const int e8v = (__float_as_uint(sv) >> 23) & 0xFF;  // power of two -> E8M0
             if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
                 const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 32 * hh;
@@ -412,27 +416,37 @@ void fwd_fp8_kernel(Fp8Args a) {
         };
 
         if (nt > 0) {
-            copy_k(0, K_OFF0);
-            copy_v(0, V_OFF0);
+            copy_k(0, lds_k0);
+            copy_v(0, lds_v0);
         }
-        if (nt > 1) copy_k(1, K_OFF1);
+        if (nt > 1) copy_k(1, lds_k1);
+        // Block scales of the tile a step works on are loaded one step ahead,
+        // before that step's tile copies: a wait for them is then never a wait
+        // for the copies (loads retire in order).  Lane half hh holds the keys
+        // of K block 2kt + hh.
+        auto kscale = [&](int kt) { return a.ks[int64_t(bh) * nkb + min(2 * kt + hh, nkb - 1)]; };
+        auto vscale = [&](int kt) { return a.vs[int64_t(bh) * nvb + min(kt, nvb - 1)]; };
+        float ks_cur = kscale(0), vs_cur = vscale(0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 sA[2], sB[2];
-        if (wnt > 0) scores(sA, smem + K_OFF0);
+        if (wnt > 0) scores(sA, lds_k0);
         __syncthreads();
 
-        auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
-                        int v_cur_off, int v_nxt_off) {
-            if (kt + 2 < nt) copy_k(kt + 2, k_cur_off);
-            if (kt + 1 < nt) copy_v(kt + 1, v_nxt_off);
-            if (kt < wnt) softmax_pv(cur, kt, smem + v_cur_off, nxt, smem + k_nxt_off);
+        auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], char* k_cur, char* k_nxt, char* v_cur,
+                        char* v_nxt) {
+            const float ks_nxt = kscale(kt + 1), vs_nxt = vscale(kt + 1);
+            if (kt + 2 < nt) copy_k(kt + 2, k_cur);
+            if (kt + 1 < nt) copy_v(kt + 1, v_nxt);
+            if (kt < wnt) softmax_pv(cur, kt, ks_cur, vs_cur, v_cur, nxt, k_nxt);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            ks_cur = ks_nxt;
+            vs_cur = vs_nxt;
         };
         for (int kt = 0; kt < nt; kt += 2) {
-            step(kt, sA, sB, K_OFF0, K_OFF1, V_OFF0, V_OFF1);
-            if (kt + 1 < nt) step(kt + 1, sB, sA, K_OFF1, K_OFF0, V_OFF1, V_OFF0);
+            step(kt, sA, sB, lds_k0, lds_k1, lds_v0, lds_v1);
+            if (kt + 1 < nt) step(kt + 1, sB, sA, lds_k1, lds_k0, lds_v1, lds_v0);
         }
 
         if (qi < a.N && wnt > 0) {
@@ -465,18 +479,9 @@ int launch_q(const QuantArgs& a, hipStream_t s) {
 template <int D, bool CAUSAL>
 int launch_a(const Fp8Args& a, hipStream_t s) {
     constexpr int NW = 8;
-    constexpr int LDS = Tile8<D>::LDS_BYTES;
-    auto kern = fwd_fp8_kernel<D, NW, CAUSAL>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr_set = true;
-    }
     const int n_qt = (a.N + NW * WQ - 1) / (NW * WQ);
     const int64_t grid = int64_t(CAUSAL ? (n_qt + 1) / 2 : n_qt) * a.B * a.H;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), LDS, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, CAUSAL>), dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
