@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "lds_copy.h"
 
 namespace fa {
 namespace {
@@ -187,7 +188,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
             const int c = blk * 64 + lane;
             const int row = c / CPR, pch = c % CPR;
             const int64_t off = int64_t(min(k0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-            __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off), (lds_void*)(ktile + blk * 1024), 16, 0, 0);
+            copy16_to_lds(Kg + off, ktile + blk * 1024);
         }
         // B operand of dO V^T: lane (key, half hh), k-step ks holds columns
         // 16ks + 8hh .. +7 of the key's V row (K comes from the LDS tile).
@@ -207,19 +208,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 const int c = blk * 64 + lane;
                 const int row = c / CPR, pch = c % CPR;
                 const int64_t roff = int64_t(min(q0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(Qg + roff),
-                                                 (lds_void*)((buf ? qtile1 : qtile0) + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(Og + roff),
-                                                 (lds_void*)((buf ? otile1 : otile0) + blk * 1024), 16, 0, 0);
+                copy16_to_lds(Qg + roff, (buf ? qtile1 : qtile0) + blk * 1024);
+                copy16_to_lds(Og + roff, (buf ? otile1 : otile0) + blk * 1024);
             }
             float* st = buf ? stat1 : stat0;
             const int qq = min(q0 + lane, a.N - 1);
             if (wave == 0)       // LSE*log2e of the 64 queries
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_lse2 + int64_t(bh) * a.N + qq),
-                                                 (lds_void*)st, 4, 0, 0);
+                copy4_to_lds(a.ws_lse2 + int64_t(bh) * a.N + qq, st);
             else if (wave == 1)  // -D
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(a.ws_nd + int64_t(bh) * a.N + qq),
-                                                 (lds_void*)(st + BQ), 4, 0, 0);
+                copy4_to_lds(a.ws_nd + int64_t(bh) * a.N + qq, st + BQ);
         };
 
         // ---- per-lane LDS offsets ----------------------------------------------
@@ -466,10 +463,8 @@ void bwd_dq_kernel(BwdArgs a) {
                 const int c = blk * 64 + lane;
                 const int row = c / CPR, pch = c % CPR;
                 const int64_t off = int64_t(min(kt * BC + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(Kg + off),
-                                                 (lds_void*)((buf ? ktile1 : ktile0) + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(Vg + off),
-                                                 (lds_void*)((buf ? vtile1 : vtile0) + blk * 1024), 16, 0, 0);
+                copy16_to_lds(Kg + off, (buf ? ktile1 : ktile0) + blk * 1024);
+                copy16_to_lds(Vg + off, (buf ? vtile1 : vtile0) + blk * 1024);
             }
         };
 

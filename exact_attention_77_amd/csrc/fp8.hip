@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "lds_copy.h"
 
 namespace fa {
 namespace {
@@ -301,7 +302,7 @@ void fwd_fp8_kernel(Fp8Args a) {
                 const int row = c / TL::KCPR, pch = c % TL::KCPR;
                 const int key = min(kt * BC + row, a.N - 1);
                 const uint8_t* g = Kg + int64_t(key) * D + 16 * (pch ^ TL::kswz(row));
-                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(dst + bk * 1024), 16, 0, 0);
+                copy16_to_lds(g, dst + bk * 1024);
             }
         };
         auto copy_v = [&](int kt, char* dst) {
@@ -309,7 +310,7 @@ void fwd_fp8_kernel(Fp8Args a) {
                 const int c = bk * 64 + lane;
                 const int row = c / 4, pch = c % 4;  // row = head-dim index
                 const uint8_t* g = Vg + int64_t(row) * npad + int64_t(kt) * BC + 16 * (pch ^ TL::vswz(row));
-                __builtin_amdgcn_global_load_lds((global_cvoid*)g, (lds_void*)(dst + bk * 1024), 16, 0, 0);
+                copy16_to_lds(g, dst + bk * 1024);
             }
         };
 

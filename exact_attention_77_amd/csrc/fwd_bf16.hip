@@ -51,6 +51,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "lds_copy.h"
 
 namespace fa {
 namespace {
@@ -160,14 +161,12 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
             const int64_t off = int64_t(k0) * a.ss;
 #pragma unroll
             for (int i = 0; i < NI; ++i)
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(src[i] + off),
-                                                 (lds_void*)(smem + lds_off + (wave * NI + i) * 1024), 16, 0, 0);
+                copy16_to_lds(src[i] + off, smem + lds_off + (wave * NI + i) * 1024);
         } else {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int64_t row_off = int64_t(min(k0 + crow[i], a.N - 1) - crow[i]);
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(src[i] + row_off * a.ss),
-                                                 (lds_void*)(smem + lds_off + (wave * NI + i) * 1024), 16, 0, 0);
+                copy16_to_lds(src[i] + row_off * a.ss, smem + lds_off + (wave * NI + i) * 1024);
             }
         }
     };
