@@ -355,6 +355,7 @@ void fwd_fp8_kernel(Fp8Args a) {
             }
         };
 
+        i32x8 pb = {};   // e4m3 probabilities of a tile: the B operand of the PV product
         auto softmax_pv = [&](f32x16 (&s)[2], int kt, float ksc, float vsc, const char* vt_lds, f32x16 (&nxt)[2],
                               const char* knext) {
             const int k_lo = kt * BC;
@@ -388,7 +389,6 @@ void fwd_fp8_kernel(Fp8Args a) {
             }
             scores(nxt, knext);
             const float bias = 6.f - m_ref;  // exp2(s*ct - m + 6) = 64 p
-            i32x8 pb;
             float ls0 = 0.f, ls1 = 0.f;
     #pragma unroll
             for (int st = 0; st < 2; ++st)
@@ -400,7 +400,10 @@ void fwd_fp8_kernel(Fp8Args a) {
                     const float p3 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 3], ct, bias));
                     ls0 += p0 + p1;
                     ls1 += p2 + p3;
-                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    // the low half is written here and the high half below, so
+                    // the incoming word is irrelevant: it is the previous tile's
+                    // (already consumed) word of the same register
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[4 * st + r], false);
                     pb[4 * st + r] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
                 }
             lsum += ls0 + ls1;
