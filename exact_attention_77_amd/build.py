@@ -20,9 +20,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function"]
+COMMON = FLAGS + ["-I", os.path.join(ROOT, "include")]
 
 # The attention kernels run with the IEEE mode bit off: v_max/v_min then need
 # no quieting of signalling NaNs, so a row maximum is one v_max3 per two
@@ -62,15 +63,25 @@ def strip_comments(text: str) -> str:
 
 
 def fingerprint(src: str) -> str:
-    """sha256 prefix of a csrc/ source file (comments, blank lines and the
-    indentation removed) plus the flags it is compiled with: it changes
-    whenever the kernel binary built from that file can change, and not for
-    an edit of its comments or layout alone."""
+    """sha256 prefix of a csrc/ source file and the csrc/ headers it includes
+    (comments, blank lines and indentation removed) plus the flags it is
+    compiled with: it changes whenever the kernel binary built from that file
+    can change, and not for an edit of comments or layout alone."""
     import hashlib
-    text = open(os.path.join(CSRC, src), encoding="utf-8").read()
-    lines = (ln.strip() for ln in strip_comments(text).splitlines())
-    h = hashlib.sha256("\n".join(ln for ln in lines if ln).encode())
-    h.update(repr((COMMON, PER_FILE.get(src, []), ARCH)).encode())
+    import re
+
+    def normalized(name):
+        text = strip_comments(open(os.path.join(CSRC, name), encoding="utf-8").read())
+        return "\n".join(ln for ln in (x.strip() for x in text.splitlines()) if ln)
+
+    body = normalized(src)
+    h = hashlib.sha256(body.encode())
+    for hdr in re.findall(r'#include\s+"([^"]+)"', body):   # the file's own headers
+        if os.path.exists(os.path.join(CSRC, hdr)):
+            h.update(normalized(hdr).encode())
+    # flags only, not the include path: the record must match wherever the
+    # tree is copied
+    h.update(repr((FLAGS, PER_FILE.get(src, []), ARCH)).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,4 +1,5 @@
 """Host-side logic of bench.py (no GPU): the HBM-traffic record lookup."""
+import importlib.util
 import json
 import os
 
@@ -62,3 +63,18 @@ def test_fingerprint_ignores_comment_edits_only(tmp_path, monkeypatch):
     assert build.fingerprint("k.hip") == f0
     (tmp_path / "k.hip").write_text("__global__ void k(int* p) { p[0] = 2; }\n")
     assert build.fingerprint("k.hip") != f0
+
+
+def test_fingerprint_does_not_depend_on_the_tree_location(tmp_path, monkeypatch):
+    """The same sources copied elsewhere (as for a run on another machine)
+    keep their fingerprint."""
+    import importlib
+    import shutil
+    from exact_attention_77_amd import build
+    f0 = build.fingerprint("fwd_bf16.hip")
+    copy = tmp_path / "elsewhere" / "exact_attention_77_amd"
+    shutil.copytree(os.path.dirname(build.__file__), copy, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    spec = importlib.util.spec_from_file_location("build_copy", copy / "build.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert mod.ROOT != build.ROOT and mod.fingerprint("fwd_bf16.hip") == f0
