@@ -307,13 +307,31 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     constexpr int PPM = NPAIR / QKM;  // pairs per score MFMA
     constexpr int NPK = 2, NPV = 2;
     static_assert(NPAIR % QKM == 0, "phase split");
+    // The last NDEF PV products of a tile are issued at the start of the next
+    // tile's block, after the workgroup barrier: the matrix core then has
+    // queued work while the next K operands are read from LDS.  Their V^T
+    // operands stay in registers (the LDS buffer they came from may be
+    // overwritten by then) and their P operand is the last chunk of pb, which
+    // the next block rewrites only later.  Before the first tile the deferred
+    // operands are zero (a product that adds exactly 0).
+    constexpr int NDEF = 2;
+    static_assert(NDEF == NPV && PVM - NDEF >= NPV, "deferred PV products");
+    bf16x8 pb[4] = {};
+    bf16x8 vdef[NDEF] = {};
+    auto flush_deferred = [&]() {
+#pragma unroll
+        for (int i = 0; i < NDEF; ++i) {
+            const int n = PVM - NDEF + i;
+            oacc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vdef[i], pb[n / DT], oacc[n % DT], 0, 0, 0);
+        }
+    };
     auto main_block = [&](f32x16 (&s)[2], const char* vt_lds, f32x16 (&nxt)[2], const char* knext) {
-        bf16x8 pb[4];
         bf16x8 kb[NPK];
 #pragma unroll
         for (int i = 0; i < NPK; ++i) kb[i] = k_operand(knext, i);
         float lpart[2] = {0.f, 0.f};  // two independent row-sum chains
         const f32x16 zero = {};
+        flush_deferred();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < QKM; ++m) {
@@ -340,12 +358,14 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         for (int i = 0; i < NPV; ++i) vb[i] = v_operand(vt_lds, i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int n = 0; n < PVM; ++n) {
+        for (int n = 0; n < PVM - NDEF; ++n) {
             const bf16x8 va = vb[n % NPV];
             if (n + NPV < PVM) vb[n % NPV] = v_operand(vt_lds, n + NPV);
             oacc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n / DT], oacc[n % DT], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int i = 0; i < NDEF; ++i) vdef[i] = vb[(PVM - NDEF + i) % NPV];
     };
 
     // ---- prologue: K0, V0, K1 in flight; S(0) ---------------------------------
@@ -381,6 +401,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         step(kt, sA, sB, K_OFF0, K_OFF1, V_OFF0, V_OFF1);
         if (kt + 1 < nt) step(kt + 1, sB, sA, K_OFF1, K_OFF0, V_OFF1, V_OFF0);
     }
+
+    flush_deferred();
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
     if (qi < a.N && wnt > 0) {
