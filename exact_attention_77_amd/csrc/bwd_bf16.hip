@@ -524,12 +524,12 @@ void bwd_dq_kernel(BwdArgs a) {
                 const char* kb_lds = kt_lds + 64 * kb * 2 * D;
                 const char* vb_lds = vt_lds + 64 * kb * 2 * D;
                 bf16x8 dsb[2][2];
-    #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    f32x16 s, dp;
+                // S^T and dP^T - D of subtile st (2*KS products alternating;
+                // LDS operands read two ahead), with the masked keys' scores
+                // set to -inf on diagonal and ragged blocks
+                auto scores = [&](int st, f32x16& s, f32x16& dp) {
     #pragma unroll
                     for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
-                    // 2*KS products alternating S^T / dP^T; LDS operands read two ahead
                     auto src = [&](int m) {
                         return ld16((m & 1) ? vb_lds : kb_lds, 32 * st * 2 * D + ro[m >> 1]);
                     };
@@ -545,18 +545,33 @@ void bwd_dq_kernel(BwdArgs a) {
                             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], qreg[m >> 1], s, 0, 0, 0);
                         __builtin_amdgcn_sched_barrier(0);
                     }
+                    if (edge) {
     #pragma unroll
-                    for (int g = 0; g < 16; ++g) {
-                        float x = fmaf(s[g], c2, -lse2);
-                        if (edge) {
+                        for (int g = 0; g < 16; ++g) {
                             const int r = g >> 2, t = g & 3;
-                            if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) x = -INFINITY;
+                            if (32 * st + 16 * (r >> 1) + 4 * (r & 1) + t > lim) s[g] = -INFINITY;
                         }
-                        dsb[st][g >> 3][g & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x) * dp[g]);
                     }
+                };
+                // dS^T = P^T (dP^T - D) for registers g0 .. g1-1 of subtile st, as bf16
+                auto ds_part = [&](int st, const f32x16& s, const f32x16& dp, int g0, int g1) {
+    #pragma unroll
+                    for (int g = g0; g < g1; ++g)
+                        dsb[st][g >> 3][g & 7] =
+                            static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[g], c2, -lse2)) * dp[g]);
+                };
+                {
+                    f32x16 s, dp;
+                    scores(0, s, dp);
+                    ds_part(0, s, dp, 0, 16);
                 }
-                // dQ^T += K^T dS^T over the block's four 16-key chunks (operands two ahead)
+                // dQ^T += K^T dS^T over the block's four 16-key chunks (operands
+                // two ahead); chunks 0 and 1 need subtile 0 only, so subtile 1's
+                // dS^T is formed beside their products
+                f32x16 s1, dp1;
+                scores(1, s1, dp1);
                 constexpr int NQ = 4 * DT;
+                constexpr int G = 16 / (2 * DT);   // subtile-1 registers per early product
                 auto tsrc = [&](int n) {
                     const int c = n / DT, dt = n % DT;
                     return ldtr(kb_lds, 16 * c * 2 * D + tro[dt][0], 16 * c * 2 * D + tro[dt][1]);
@@ -570,6 +585,7 @@ void bwd_dq_kernel(BwdArgs a) {
                     if (n + 2 < NQ) top[(n + 2) % 3] = tsrc(n + 2);
                     const int c = n / DT, dt = n % DT;
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[n % 3], dsb[c >> 1][c & 1], acc[dt], 0, 0, 0);
+                    if (n < 2 * DT) ds_part(1, s1, dp1, G * n, G * (n + 1));
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
