@@ -267,12 +267,36 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int n_qt = (a.N + BQ - 1) / BQ;
         const int qt0 = CAUSAL ? k0 / BQ : 0;
 
+        // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1) over the tile's 64
+        // queries: 16-query chunk c, head-dim tile dt.  The A operand is read
+        // transposed from the tile's Q or dO buffer, the B operand (P^T or
+        // dS^T rows of this wave's keys) from the exchange buffer.
+        constexpr int NP = BQ / 16 * DT;   // products per tile
+        constexpr int NEARLY = NP / 2;     // issued in the tile's own step
+        constexpr int NLATE = NP - NEARLY; // issued in the next step, beside its vector work
+        auto a_operand = [&](const char* at, int n) {
+            const int c = n / DT, dt = n % DT;
+            return ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
+        };
+        const int BO = qh ? PT_BYTES : 0;
+        bf16x8 late_b[NLATE / DT];   // B operands of the deferred chunks (read before the barrier)
+        // the deferred products of the previous tile, A operands from its buffer
+        // (not overwritten before this step's prefetch), n = NEARLY .. NP-1
+        auto late_mfma = [&](const char* at_prev, int i, bf16x8 (&op)[3]) {
+            const int n = NEARLY + i;
+            if (i + 2 < NLATE) op[(i + 2) % 3] = a_operand(at_prev, n + 2);
+            acc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], late_b[n / DT - NEARLY / DT], acc[n % DT], 0, 0, 0);
+        };
+
         if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
         // One query tile; `bufc` carries the LDS buffer as a compile-time constant
         // (the loop below is unrolled by two) so that the compiler can tell the
         // prefetch target from the buffer being read and does not wait for it.
-        auto step = [&](int it, auto bufc) {
+        // With `latec` true the previous tile (in the other buffer) left NLATE
+        // products to this step.
+        auto step = [&](int it, auto bufc, auto latec) {
             constexpr int buf = decltype(bufc)::value;
+            constexpr bool LATE = decltype(latec)::value;
             const int qt_base = it * BQ;
             const int q0 = qt_base + 32 * qh;         // first query of this wave
             // tile `it` is in LDS; every wave is done with the previous P^T / dS^T
@@ -280,6 +304,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
             __builtin_amdgcn_s_barrier();
             const char* qt = buf ? qtile1 : qtile0;
             const char* ot = buf ? otile1 : otile0;
+            const char* at_prev = qh ? (buf ? qtile0 : qtile1) : (buf ? otile0 : otile1);
             const float* ls = (buf ? stat1 : stat0) + 32 * qh;
 
             // S = Q K^T and dP - D (register g = 4r + t of lane half hh: query
@@ -312,16 +337,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 }
             }
 
-            // P = exp2(S c - LSE log2 e), zero for masked (query, key) pairs
-            float p[16];
-    #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float4 l2 = *reinterpret_cast<const float4*>(ls + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
-                p[4 * r + 0] = fmaf(s[4 * r + 0], c2, -l2.x);
-                p[4 * r + 1] = fmaf(s[4 * r + 1], c2, -l2.y);
-                p[4 * r + 2] = fmaf(s[4 * r + 2], c2, -l2.z);
-                p[4 * r + 3] = fmaf(s[4 * r + 3], c2, -l2.w);
-            }
+            // masked (query, key) pairs get score -inf, hence P = 0
             const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 32 > a.N || kw0 + 32 > a.N;
             if (edge) {  // wave-uniform: diagonal or ragged blocks only
                 const int lo = CAUSAL ? key - q0 - 8 * hh : -(1 << 30);
@@ -330,18 +346,37 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 for (int g = 0; g < 16; ++g) {
                     const int r = g >> 2, t = g & 3;
                     const int off = 16 * (r >> 1) + 4 * (r & 1) + t;
-                    if (off < lo || off > hi) p[g] = -INFINITY;
+                    if (off < lo || off > hi) s[g] = -INFINITY;
                 }
             }
-            // P and dS = P (dP - D) as bf16, stored transposed (row = key) for the
-            // products over the whole 64-query tile
-            bf16x8 pb[2], dsb[2];
+            float l2[16];
     #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                p[g] = __builtin_amdgcn_exp2f(p[g]);
-                pb[g >> 3][g & 7] = static_cast<__bf16>(p[g]);
-                dsb[g >> 3][g & 7] = static_cast<__bf16>(p[g] * dp[g]);
+            for (int r = 0; r < 4; ++r) {
+                const float4 v4 = *reinterpret_cast<const float4*>(ls + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
+                l2[4 * r + 0] = v4.x; l2[4 * r + 1] = v4.y; l2[4 * r + 2] = v4.z; l2[4 * r + 3] = v4.w;
             }
+            // P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16, in fenced
+            // chunks beside the previous tile's deferred products
+            bf16x8 pb[2], dsb[2];
+            bf16x8 lop[3];
+            if constexpr (LATE) {
+                lop[0] = a_operand(at_prev, NEARLY);
+                lop[1] = a_operand(at_prev, NEARLY + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int GPC = 16 / NLATE;   // registers per chunk
+    #pragma unroll
+            for (int i = 0; i < NLATE; ++i) {
+                if constexpr (LATE) late_mfma(at_prev, i, lop);
+    #pragma unroll
+                for (int g = GPC * i; g < GPC * (i + 1); ++g) {
+                    const float pg = __builtin_amdgcn_exp2f(fmaf(s[g], c2, -l2[g]));
+                    pb[g >> 3][g & 7] = static_cast<__bf16>(pg);
+                    dsb[g >> 3][g & 7] = static_cast<__bf16>(pg * dp[g]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // stored transposed (row = key) for the products over the whole 64-query tile
     #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 *reinterpret_cast<bf16x8*>(ptbuf + pwo[c]) = pb[c];
@@ -349,41 +384,56 @@ void bwd_dkdv_kernel(BwdArgs a) {
             }
             // Prefetch the next tile once this iteration's LDS stores are issued
             // (LDS stores behind a pending direct-to-LDS load get made to wait).
+            // The deferred products above were the last readers of its buffer.
             if (it + 1 < n_qt) copy_q(qt_base + BQ, std::integral_constant<int, buf ^ 1>{});
             // P^T and dS^T of the whole tile are in LDS (LDS stores only: the
             // prefetch just issued stays in flight across this barrier)
             __builtin_amdgcn_s_waitcnt(kWaitLds);
             __builtin_amdgcn_s_barrier();
 
-            // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1), over 64 queries
-            auto tile_product = [&](const char* at, auto bo) {
-                constexpr int BO = decltype(bo)::value;
-                constexpr int NP = BQ / 16 * DT;   // products; A operands read two ahead
-                auto src = [&](int n) {
-                    const int c = n / DT, dt = n % DT;
-                    return ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
-                };
-                bf16x8 op[3], bop = ld16(ptbuf, pto[0] + BO);
-                op[0] = src(0);
-                op[1] = src(1);
-                __builtin_amdgcn_sched_barrier(0);
+            // the first NEARLY products now; the B operands of the rest are read
+            // here too, as the next step overwrites the exchange buffer
+            const char* at = qh ? qt : ot;
+            bf16x8 op[3], bop = ld16(ptbuf, pto[0] + BO);
+            op[0] = a_operand(at, 0);
+            op[1] = a_operand(at, 1);
     #pragma unroll
-                for (int n = 0; n < NP; ++n) {
-                    if (n + 2 < NP) op[(n + 2) % 3] = src(n + 2);
-                    const int c = n / DT, dt = n % DT;
-                    const bf16x8 b = bop;
-                    if (dt == DT - 1 && c + 1 < BQ / 16) bop = ld16(ptbuf, pto[c + 1] + BO);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], b, acc[dt], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            };
-            if (qh) tile_product(qt, std::integral_constant<int, PT_BYTES>{});
-            else    tile_product(ot, std::integral_constant<int, 0>{});
-
+            for (int i = 0; i < NLATE / DT; ++i) late_b[i] = ld16(ptbuf, pto[NEARLY / DT + i] + BO);
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int n = 0; n < NEARLY; ++n) {
+                if (n + 2 < NEARLY) op[(n + 2) % 3] = a_operand(at, n + 2);
+                const int c = n / DT, dt = n % DT;
+                const bf16x8 b = bop;
+                if (dt == DT - 1 && c + 1 < NEARLY / DT) bop = ld16(ptbuf, pto[c + 1] + BO);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], b, acc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
-        for (int it = qt0; it < n_qt; it += 2) {
-            step(it, std::integral_constant<int, 0>{});
-            if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
+        // the deferred products of the last tile (buffer `bufc`)
+        auto flush = [&](auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+            const char* at = qh ? (buf ? qtile1 : qtile0) : (buf ? otile1 : otile0);
+            bf16x8 lop[3];
+            lop[0] = a_operand(at, NEARLY);
+            lop[1] = a_operand(at, NEARLY + 1);
+    #pragma unroll
+            for (int i = 0; i < NLATE; ++i) late_mfma(at, i, lop);
+        };
+        if (qt0 < n_qt) {
+            // the first tile has no deferred products before it
+            step(qt0, std::integral_constant<int, 0>{}, std::false_type{});
+            int it = qt0 + 1;
+            for (; it + 1 < n_qt; it += 2) {
+                step(it, std::integral_constant<int, 1>{}, std::true_type{});
+                step(it + 1, std::integral_constant<int, 0>{}, std::true_type{});
+            }
+            if (it < n_qt) {
+                step(it, std::integral_constant<int, 1>{}, std::true_type{});
+                flush(std::integral_constant<int, 1>{});
+            } else {
+                flush(std::integral_constant<int, 0>{});
+            }
         }
 
         // ---- epilogue: dV (qh = 0) or dK = scale * (dK^T)^T (qh = 1), bf16 -------
