@@ -25,13 +25,18 @@
 //              then the wave of query half 0 accumulates dV^T += dO^T P and
 //              the one of half 1 dK^T += Q^T dS over the whole 64-query tile
 //              (dO^T, Q^T by transposing LDS reads; P^T, dS^T by row reads).
+//              Half of those products is issued in the next tile's step,
+//              beside its exp/dS work, so that this vector work has matrix
+//              work next to it.
 //  3. dQ   : one workgroup per (batch, head, 256-query tile), eight waves of
 //            32 queries, K/V tiles of 64 keys streamed through LDS (the loop
 //            order of the forward pass).  Per tile the transposed products
 //            S^T = K Q^T and dP^T - D = V dO^T (Q^T, dO^T held in registers)
 //            put one query per lane, dS^T = P^T (dP^T - D) -> bf16 is, with K
 //            rows fed in a permuted order, directly the B operand of
-//            dQ^T += K^T dS^T, and dQ is written once at the end.
+//            dQ^T += K^T dS^T, and dQ is written once at the end.  The dS^T of
+//            a block's second 32-key subtile is formed beside the dQ products
+//            of its first subtile.
 // dQ is thus computed by recomputing S and dP per query tile instead of being
 // summed over key tiles with atomic adds: 40% more matrix work, but the fp32
 // atomics into a shared accumulator cost more than that on this chip (their
