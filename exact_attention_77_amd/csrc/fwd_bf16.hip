@@ -457,13 +457,10 @@ int launch(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = NW * WQ;
     constexpr int LDS = Tile<D>::LDS_BYTES;
     auto kern = fwd_bf16_kernel<D, NW, CAUSAL>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr_set = true;
-    }
+    // set once per process (thread-safe initialisation of a local static)
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess) return static_cast<int>(attr);
     const int n_qt = (a.N + BR - 1) / BR;
     const int64_t grid = int64_t(CAUSAL ? (n_qt + 1) / 2 : n_qt) * a.B * a.H;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(NW * 64), LDS, stream, a);

@@ -16,9 +16,11 @@
  *
  * Conventions shared by every entry point.
  *  - Pointers to tensors are DEVICE pointers owned by the caller; the library
- *    allocates no device memory, keeps no mutable global state and never
- *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
- *    default stream) and the caller synchronises.
+ *    allocates no device memory and never synchronises: work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and the caller
+ *    synchronises.  Its only state is a per-thread last-error message and a
+ *    kernel attribute (the bf16 forward's LDS size) set once per process, so
+ *    concurrent calls from several host threads are safe.
  *  - Arguments are validated on the host before any HIP call; on any error
  *    return nothing is enqueued and the outputs are untouched.  A failed kernel
  *    launch returns FLASH_ATTN_ERR_HIP; flash_attn_last_error() then describes it.
