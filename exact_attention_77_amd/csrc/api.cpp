@@ -21,6 +21,7 @@ flash_attn_status hip_status(int err) {
 }
 
 constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxTotalRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxMergeParts = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -36,6 +37,8 @@ flash_attn_status check_shape(const flash_attn_layout& L) {
     if (L.seqlen > kMaxRows) return FLASH_ATTN_ERR_SHAPE;
     if (L.batch > kMaxRows || L.heads > kMaxRows || L.batch * L.heads > kMaxRows)
         return FLASH_ATTN_ERR_SHAPE;
+    // every row index and the kernels' work decompositions stay in int32
+    if (L.batch * L.heads * L.seqlen > kMaxTotalRows) return FLASH_ATTN_ERR_SHAPE;
     if (is_empty(L)) return FLASH_ATTN_OK;
     if (L.head_dim != 64 && L.head_dim != 128) return FLASH_ATTN_ERR_UNSUPPORTED;
     return FLASH_ATTN_OK;

@@ -65,7 +65,8 @@ typedef enum flash_attn_dtype {
 } flash_attn_dtype;
 
 /* Shape and strides (in elements) shared by Q, K, V and O.
- * Limits: 0 <= batch*heads <= 2^24, 0 <= seqlen <= 2^24. */
+ * Limits: 0 <= batch*heads <= 2^24, 0 <= seqlen <= 2^24 and
+ * batch*heads*seqlen < 2^31 (beyond any tensor the device can hold). */
 typedef struct flash_attn_layout {
     int64_t batch, heads, seqlen, head_dim;
     int64_t stride_b, stride_h, stride_s;

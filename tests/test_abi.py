@@ -69,7 +69,10 @@ def test_empty_inputs_are_noops():
 
 
 @pytest.mark.parametrize("lay", [_lay(N=-1), _lay(B=-2), _lay(N=(1 << 24) + 1),
-                                 fa.Layout(1 << 13, 1 << 12, 16, 64, 64, 64, 64)])
+                                 fa.Layout(1 << 13, 1 << 12, 16, 64, 64, 64, 64),
+                                 # each size within its limit, the row count 2^32 beyond int32
+                                 fa.Layout(1 << 12, 1 << 12, 1 << 8, 64, 64, 64, 64),
+                                 fa.Layout(1, 1 << 8, 1 << 24, 64, 64, 64, 64)])
 def test_bad_shapes(lay):
     assert fwd(lay=lay) == 2
 
