@@ -175,3 +175,15 @@ def test_full_size_workload_sampled(name):
     rows = sample_rows(w.B, w.H, w.N, 1024, w.seed)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     _check(o, lse, ref, w.causal, "bf16", rows=rows)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_sampled(causal):
+    """N = 65536, eight times the longest workload: 1024 key tiles per head,
+    so long chains of online-softmax updates; seeded rows (including the
+    first and last rows of both heads) against the oracle."""
+    B, H, N, d = 1, 2, 65536, 128
+    dev, ref = _inputs(B, H, N, d, 11, "bf16")
+    o, lse = _run(dev, causal)
+    rows = sample_rows(B, H, N, 256, 11)
+    _check(o, lse, ref, causal, "bf16", rows=rows)
