@@ -12,8 +12,9 @@
 // the per-row statistic the forward stored (its natural-log LSE, so that
 // P_ij = exp(s_ij - LSE_i)).
 //
-// Three kernels, all on the caller's stream:
-//  1. prep : per query row, -D_i and LSE_i * log2(e) (fp32) into the workspace.
+// Two kernels, both on the caller's stream, the dQ kernel first:
+//  1. dQ   : (below) also forms, per query row, -D_i and LSE_i * log2(e) (fp32)
+//            and stores them in the workspace for the dK/dV kernel.
 //  2. dK/dV: one workgroup per (batch, head, 128-key tile), eight waves; wave
 //            w works on key block w % 4 (32 keys) and query half w / 4 of each
 //            64-query tile of Q and dO, staged in LDS by direct global->LDS
@@ -28,9 +29,11 @@
 //              Half of those products is issued in the next tile's step,
 //              beside its exp/dS work, so that this vector work has matrix
 //              work next to it.
-//  3. dQ   : one workgroup per (batch, head, 256-query tile), eight waves of
+//  dQ kernel: one workgroup per (batch, head, 256-query tile), eight waves of
 //            32 queries, K/V tiles of 64 keys streamed through LDS (the loop
-//            order of the forward pass).  Per tile the transposed products
+//            order of the forward pass); each query row belongs to exactly one
+//            lane pair, which forms D_i from the row's dO (already in its
+//            registers) and O.  Per tile the transposed products
 //            S^T = K Q^T and dP^T - D = V dO^T (Q^T, dO^T held in registers)
 //            put one query per lane, dS^T = P^T (dP^T - D) -> bf16 is, with K
 //            rows fed in a permuted order, directly the B operand of
@@ -101,36 +104,7 @@ __device__ __forceinline__ bf16x8 cat(short4_t lo, short4_t hi) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. prep: D/8 lanes per query row.  -D and LSE*log2e are what the two main
-// kernels add to their score accumulators.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-    constexpr int LPR = D / 8;
-    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t row = t / LPR;                 // flat (b, h, i)
-    const int l = static_cast<int>(t % LPR);
-    const int64_t rows = int64_t(a.B) * a.H * a.N;
-    if (row >= rows) return;
-    const int i = static_cast<int>(row % a.N);
-    const int64_t bh = row / a.N;
-    const int b = static_cast<int>(bh / a.H), h = static_cast<int>(bh % a.H);
-    const int64_t off = int64_t(b) * a.sb + int64_t(h) * a.sh + int64_t(i) * a.ss + 8 * l;
-    const uint4 ov = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.o) + off);
-    const uint4 gv = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.dout) + off);
-    const bf16x8 o8 = __builtin_bit_cast(bf16x8, ov), g8 = __builtin_bit_cast(bf16x8, gv);
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(o8[e]), static_cast<float>(g8[e]), acc);
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, LPR);
-    if (l == 0) {
-        a.ws_nd[row] = -acc;
-        a.ws_lse2[row] = a.lse[row] * kLog2e;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dK/dV kernel: 8 waves; wave w works on key block kb = w % 4 (32 keys) and
+// dK/dV kernel: 8 waves; wave w works on key block kb = w % 4 (32 keys) and
 // query half qh = w / 4 (32 of the tile's 64 queries) for S, dP, P and dS; the
 // wave with qh = 0 accumulates dV of its key block, the one with qh = 1 dK.
 template <int D, bool CAUSAL>
@@ -460,7 +434,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ kernel: NW waves of 32 queries, BC-key K/V tiles double-buffered
+// dQ kernel: NW waves of 32 queries, BC-key K/V tiles double-buffered
 // (processed in 64-key blocks).
 template <int D, bool CAUSAL, int NW, int BC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
@@ -536,8 +510,27 @@ void bwd_dq_kernel(BwdArgs a) {
             qreg[ks] = __builtin_bit_cast(bf16x8, xq);
             oreg[ks] = __builtin_bit_cast(bf16x8, xo);
         }
-        const float lse2 = qi < a.N ? a.ws_lse2[int64_t(bh) * a.N + qi] : 0.f;
-        const float nd = qi < a.N ? a.ws_nd[int64_t(bh) * a.N + qi] : 0.f;
+        // -D_i = -sum_c dO_ic O_ic (O as the forward stored it) and LSE_i log2(e):
+        // lane half hh holds half of the row's columns of dO, so it sums the
+        // products of that half and adds its partner lane's (l ^ 32) sum.
+        // Stored for the dK/dV kernel, which runs after this one.
+        float dpart = 0.f;
+        if (qi < a.N) {
+            const u16* Orow = static_cast<const u16*>(a.o) + base + int64_t(qi) * a.ss;
+    #pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 o8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Orow + 16 * ks + 8 * hh));
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) dpart = fmaf(static_cast<float>(o8[e]), static_cast<float>(oreg[ks][e]), dpart);
+            }
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart), __float_as_uint(dpart), false, false);
+        const float nd = -(__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+        const float lse2 = qi < a.N ? a.lse[int64_t(bh) * a.N + qi] * kLog2e : 0.f;
+        if (qi < a.N && hh == 0) {
+            a.ws_nd[int64_t(bh) * a.N + qi] = nd;
+            a.ws_lse2[int64_t(bh) * a.N + qi] = lse2;
+        }
 
         // ---- per-lane LDS offsets ----------------------------------------------
         const int prow = perm_row(j);                                  // K / V row operand (+32 st)
@@ -677,20 +670,19 @@ void bwd_dq_kernel(BwdArgs a) {
 
 template <int D>
 int run(const BwdArgs& a, hipStream_t s) {
-    const int64_t threads = int64_t(a.B) * a.H * a.N * (D / 8);
-    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
+    // the dQ kernel first: it also writes the per-row statistics the dK/dV
+    // kernel reads
+    constexpr int NW = 8, BC = 128;   // dQ kernel: 256 queries per workgroup, 128-key tiles
+    const int n_qt = (a.N + 32 * NW - 1) / (32 * NW);
+    const unsigned g_q = static_cast<unsigned>(int64_t(a.causal ? (n_qt + 1) / 2 : n_qt) * a.B * a.H);
+    if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
     int err = static_cast<int>(hipGetLastError());
     if (err) return err;
     const int n_kt = (a.N + BK - 1) / BK;
     const unsigned g_kv = static_cast<unsigned>(int64_t(a.causal ? (n_kt + 1) / 2 : n_kt) * a.B * a.H);
     if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(512), 0, s, a);
-    if ((err = static_cast<int>(hipGetLastError()))) return err;
-    constexpr int NW = 8, BC = 128;   // dQ kernel: 256 queries per workgroup, 128-key tiles
-    const int n_qt = (a.N + 32 * NW - 1) / (32 * NW);
-    const unsigned g_q = static_cast<unsigned>(int64_t(a.causal ? (n_qt + 1) / 2 : n_qt) * a.B * a.H);
-    if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, false, NW, BC>), dim3(g_q), dim3(64 * NW), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
