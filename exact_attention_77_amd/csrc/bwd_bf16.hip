@@ -208,9 +208,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
         const int tr_half = 8 * (lane & 1);
         // P^T / dS^T: 128-byte rows (64 queries) of 8-byte pieces; the 16-byte
-        // chunk is XOR-swizzled by row so that per-key row reads (16 lanes, 16
-        // keys) and transposing reads (4 consecutive keys) are conflict-free.
-        auto pt_swz = [](int row) { return 2 * (4 * ((row >> 1) & 1) + ((row >> 2) & 3)); };
+        // chunk is XOR-swizzled by row (key).  Lanes 0..31 of a wave write or
+        // read one chunk of rows 0..31: eight consecutive keys get eight
+        // different chunks (the 16-byte writes go eight lanes at a time), and
+        // in sixteen consecutive keys no two of the same parity share a chunk
+        // (what the 16-byte row reads need).  Measured: no LDS bank conflicts.
+        auto pt_swz = [](int row) { return 2 * ((row & 7) ^ ((row >> 3) & 1)); };
         int qo[KS], ko[KS];           // row operands: Q/dO rows prow, K rows krow
     #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
