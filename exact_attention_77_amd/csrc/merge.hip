@@ -45,23 +45,48 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.lse_parts[int64_t(s) * rows + row]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float total = 0.f;
+    // the lane's 8 columns of part s, as floats
+    auto load = [&](int s, float (&x)[8]) {
+        const int64_t po = int64_t(s) * a.part_stride + off;
+        if (BF16) {
+            const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                            static_cast<const u16*>(a.o_parts) + po));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
+        } else {
+            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.o_parts) + po);
+            const float4 x0 = p[0], x1 = p[1];
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+        }
+    };
+    auto weight = [&](int s) {
+        return __builtin_amdgcn_exp2f((a.lse_parts[int64_t(s) * rows + row] - m) * kLog2e);
+    };
     if (m != -INFINITY) {
-        for (int s = 0; s < a.S; ++s) {
-            const float w = __builtin_amdgcn_exp2f((a.lse_parts[int64_t(s) * rows + row] - m) * kLog2e);
-            total += w;
-            const int64_t po = int64_t(s) * a.part_stride + off;
-            if (BF16) {
-                const bf16x8 x = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                                                static_cast<const u16*>(a.o_parts) + po));
+        // four parts' loads in flight before their products (the stream is
+        // bound by how many bytes each lane keeps outstanding)
+        constexpr int U = 4;
+        int s = 0;
+        for (; s + U <= a.S; s += U) {
+            float x[U][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, static_cast<float>(x[e]), acc[e]);
-            } else {
-                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.o_parts) + po);
-                const float4 x0 = p[0], x1 = p[1];
-                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            for (int u = 0; u < U; ++u) load(s + u, x[u]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, xs[e], acc[e]);
+            for (int u = 0; u < U; ++u) {
+                const float w = weight(s + u);
+                total += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
             }
+        }
+        for (; s < a.S; ++s) {
+            float x[8];
+            load(s, x);
+            const float w = weight(s);
+            total += w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
         }
     }
     // no key in any part: O = 0, LSE = -inf
