@@ -59,7 +59,7 @@ def _compare(o, lse, o_ref, l_ref, tol_o):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 37, 300])
-@pytest.mark.parametrize("S", [1, 2, 3, 8])
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 7, 8])
 def test_merge_parity(S, N, d, dtype):
     o_parts, lse_parts, ref_o, ref_l = _parts(S, 2, 3, N, d, 100 * S + N + d, dtype,
                                               empty_rows=(N - 1,) if N > 5 else ())
