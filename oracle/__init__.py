@@ -15,8 +15,10 @@ Low-precision" sec. 技術 3 / 数値誤差.
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force in 50-digit arithmetic (mpmath) and
 library routines (torch fp64 SDPA, torch.float8_e4m3fn, scipy's Hadamard).
-The fp8 P-quantisation rule (``p_quant=1``) is a reading of a silent point; its
-arithmetic is pinned by the codec tests, its choice is "parity unpinned".
+The fp8 P-quantisation rule of the per-tensor baseline (``p_quant=1``:
+e4m3(256 p)/256 in the product with V, the row sum of the unquantised p) is a
+reading of a point the pages leave open; its arithmetic is pinned by closed
+forms on exactly representable inputs (tests/test_oracle_fp8.py).
 """
 from __future__ import annotations
 

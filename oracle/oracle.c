@@ -82,8 +82,8 @@ static void attn_row(const double* q_row, const double* kh, const double* vh,
     for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
     for (int64_t j = 0; j < n_allowed; ++j) {
         const double p = exp(s[j] - m);
-        l += p;
         const double pw = p_quant ? e4m3_decode_one(e4m3_encode_one(p * 256.0)) / 256.0 : p;
+        l += p;
         for (int64_t c = 0; c < d; ++c) o_row[c] += pw * vh[j * d + c];
     }
     for (int64_t c = 0; c < d; ++c) o_row[c] /= l;

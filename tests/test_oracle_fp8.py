@@ -131,3 +131,55 @@ def test_quantize_blocks_pow2_scales():
     y = np.zeros((1, 1, 4, 4)); y[0, 0, 0, 0] = 448.0 * 2.0 ** -3
     _, s2 = oracle.quantize_blocks(y, 4, pow2=True)
     assert s2[0, 0, 0] == 2.0 ** -3
+
+
+# ---- the per-tensor fp8 baseline's probability path, by closed forms ----
+# "FlashAttention-3: ...", 数値誤差: the comparison baseline is standard
+# attention with per-tensor fp8 scaling.  Its probabilities enter the product
+# with V as e4m3(256 p) / 256 while the row sum keeps the unquantised p (a
+# reading of a point the page leaves open).  Inputs below are chosen so that
+# every quantised operand is exact (amax 448 gives the per-tensor scale 1 and
+# every entry is an e4m3 value), so the expected results are hand-written.
+
+def test_per_tensor_baseline_zero_q_gives_mean_of_v():
+    # Q = 0: every score is 0, every p = 1 and e4m3(256)/256 = 1 exactly.
+    v = np.array([[448.0, -3.0], [0.5, 12.0], [-0.25, 1.125], [7.0, -448.0], [2.0, 0.0]])
+    q = np.zeros((1, 1, 5, 2))
+    k = np.random.default_rng(4).standard_normal((1, 1, 5, 2))
+    o, lse = oracle.fp8_per_tensor_baseline(q, k, v[None, None])
+    assert np.max(np.abs(o[0, 0] - v.mean(axis=0))) <= 1e-13
+    assert np.max(np.abs(lse - np.log(5.0))) <= 1e-15
+
+
+def _two_key_case(p1):
+    """q = (448, 0), keys (0, 0) and (-448, 0), scale = -ln(p1)/448^2: the
+    scores are 0 and ln(p1), so the probabilities are 1 and p1."""
+    q = np.array([[[[448.0, 0.0]]]])
+    k = np.array([[[[0.0, 0.0], [-448.0, 0.0]]]])
+    v = np.array([[[[448.0, 1.0], [-16.0, 3.0]]]])
+    scale = -np.log(p1) / 448.0 ** 2
+    # a single query row: repeat the query so that Q, K, V share one shape
+    q2 = np.concatenate([q, q], axis=2)
+    return q2, k, v, scale
+
+
+@pytest.mark.parametrize("kexp", [0, 3, 9, 17])
+def test_per_tensor_baseline_power_of_two_probabilities(kexp):
+    # p1 = 2^-k: 256 p1 is an e4m3 value for k <= 17 (2^-9 is the smallest
+    # subnormal), so R1 = (v0 + 2^-k v1) / (1 + 2^-k) exactly.
+    p1 = 2.0 ** -kexp
+    q, k, v, scale = _two_key_case(p1)
+    o, lse = oracle.fp8_per_tensor_baseline(q, k, v, scale=scale)
+    want = (v[0, 0, 0] + p1 * v[0, 0, 1]) / (1.0 + p1)
+    assert np.max(np.abs(o[0, 0, 0] - want)) <= 1e-12
+    assert abs(lse[0, 0, 0] - np.log(1.0 + p1)) <= 1e-12
+
+
+def test_per_tensor_baseline_rounds_p_not_the_row_sum():
+    # p1 = 0.3: 256 * 0.3 = 76.8 lies between the e4m3 values 72 and 80 and
+    # rounds to 80, so the weight of key 1 is 80/256 = 0.3125 while the row
+    # sum keeps 1 + 0.3.
+    q, k, v, scale = _two_key_case(0.3)
+    o, _ = oracle.fp8_per_tensor_baseline(q, k, v, scale=scale)
+    want = (v[0, 0, 0] + 0.3125 * v[0, 0, 1]) / 1.3
+    assert np.max(np.abs(o[0, 0, 0] - want)) <= 1e-12

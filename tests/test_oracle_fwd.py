@@ -41,6 +41,39 @@ def test_probability_rows_sum_to_one(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_reproduce_the_forward(causal):
+    """A probability row times V is the output row of the forward oracle (whose
+    pins are below), and its log-normaliser is the forward's LSE: the row
+    P[i, :] = exp(s_i - LSE_i) is what O = P V and LSE summarise."""
+    q, k, v = _qkv(2, 3, 37, 16, 21)
+    B, H, N, d = q.shape
+    o, lse = oracle.attn_fwd(q, k, v, causal=causal)
+    for flat in [0, 1, 17, N - 1, N + 5, 2 * N + 30, B * H * N - 1]:
+        bh, i = divmod(flat, N)
+        b, h = divmod(bh, H)
+        p = oracle.attn_probs_row(q, k, flat, causal=causal)
+        assert np.max(np.abs(p @ v[b, h] - o[b, h, i])) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_brute_force_mpmath(causal):
+    import mpmath as mp
+    mp.mp.dps = 50
+    g = np.random.default_rng(31)
+    q, k = (g.standard_normal((1, 2, 5, 3)) * 2 for _ in range(2))
+    scale = 0.9
+    for flat in range(10):
+        h, i = divmod(flat, 5)
+        js = range(i + 1) if causal else range(5)
+        s = {j: mp.mpf(scale) * mp.fsum(mp.mpf(q[0, h, i, c]) * mp.mpf(k[0, h, j, c]) for c in range(3))
+             for j in js}
+        z = mp.fsum(mp.e ** s[j] for j in js)
+        want = np.array([float(mp.e ** s[j] / z) if j in s else 0.0 for j in range(5)])
+        got = oracle.attn_probs_row(q, k, flat, causal=causal, scale=scale)
+        assert np.max(np.abs(got - want)) <= 1e-15
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_constant_v_returns_constant(causal):
     q, k, _ = _qkv(1, 2, 50, 8, 12)
     c = np.linspace(-3, 5, 8)

@@ -28,6 +28,12 @@ MUTANTS = {
     "e4m3_ties_down": ("else pick = (lo % 2 == 0) ? lo : lo + 1;", "else pick = lo;", "test_oracle_fp8.py"),
     "e4m3_bias": ("else mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
                   "else mag = ldexp(1.0 + (double)m / 8.0, e - 8);", "test_oracle_fp8.py"),
+    "r1_p_unscaled": ("e4m3_decode_one(e4m3_encode_one(p * 256.0)) / 256.0 : p;",
+                      "e4m3_decode_one(e4m3_encode_one(p * 256.0)) : p;", "test_oracle_fp8.py"),
+    "r1_sum_of_quantised_p": ("l += p;", "l += pw;", "test_oracle_fp8.py"),
+    "probs_dropped_scale": ("p_out[j] = scale * acc;", "p_out[j] = acc;", "test_oracle_fwd.py"),
+    "probs_wrong_row": ("acc += q[flat_row * d + c] * kh[j * d + c];",
+                        "acc += q[(flat_row ^ 1) * d + c] * kh[j * d + c];", "test_oracle_fwd.py"),
     "hadamard_no_signs": ("acc += x[r * d + i] * (double)signs[i] * hadamard_entry(i, j);",
                           "acc += x[r * d + i] * hadamard_entry(i, j);", "test_oracle_fp8.py"),
 }
