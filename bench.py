@@ -11,10 +11,13 @@ TFLOP/s of the kernel against the dense bf16 MFMA peak, timed with HIP events
 on the stream the kernel runs on) and a "cpu_baseline" object (the fp64 oracle
 timed on a bounded sample of the same workload's heads on the host cores).
 
-The default warm-up (300 launches, about 0.2 s of back-to-back work for the
-headline workload) is there because the chip's clock settles only after tens
-of milliseconds of sustained MFMA load: launches in the first ~50 ms run up to
-20% slower than the steady state that the timed 200 launches then measure.
+Before the W warm-up steps a settle phase runs back-to-back launches for about
+--settle-ms of GPU time (default 300 ms) and is reported under "settle": the
+chip's clock settles only after tens of milliseconds of sustained MFMA load,
+and launches in the first ~50 ms run up to 20% slower than the steady state
+that the K timed steps then measure.  The settle phase is untimed extra
+warm-up; W and K keep their exact meaning, and every timed step does the
+whole call.
 """
 from __future__ import annotations
 
@@ -39,6 +42,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="back-to-back launches for about this much GPU time before the "
+                         "warm-up, so the clock has settled (reported as 'settle')")
     ap.add_argument("--workload", default="bf16_causal_n8192_d128")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -105,6 +111,37 @@ def device_info():
     return info
 
 
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def settle(step, target_ms):
+    """Back-to-back launches, in timed batches of 20, until about target_ms of
+    GPU time has passed, so that the clock has reached its sustained level
+    before the warm-up and the timed steps.  Reported in the output line;
+    never part of the timed region."""
+    import torch
+
+    total, launches = 0.0, 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while total < target_ms and launches < 100000:
+        e0.record()
+        for _ in range(20):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+        launches += 20
+    return {"ms": round(total, 2), "launches": launches}
+
+
 def cpu_baseline(w, target_s):
     """Time the fp64 oracle on a bounded, seeded sample of the workload: whole
     (batch, head) slices in a seeded order until about target_s of wall time."""
@@ -113,6 +150,7 @@ def cpu_baseline(w, target_s):
     import oracle
     from synth_inputs import normal_qkv, to_bf16
 
+    oracle.use_native_build()
     if w.backward:
         q, k, v, dout = normal_qkv(w.B, w.H, w.N, w.d, w.seed, with_dout=True)
     else:
@@ -136,7 +174,8 @@ def cpu_baseline(w, target_s):
         if t_total >= target_s:
             break
     return {"value": done * flops_per_head / t_total / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(t_total, 3),
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "build": "gcc -O3 -march=native -fopenmp",
+            "kind": "oracle", "seconds": round(t_total, 3),
             "sample": f"{done} of {w.B * w.H} (batch, head) slices of the workload, every row, "
                       + ("fp64 analytic gradient, OpenMP over rows" if w.backward
                          else "fp64 two-pass, OpenMP over rows")}
@@ -239,11 +278,12 @@ def main():
             fa.flash_attn_fwd(*tens, causal=w.causal, scale=w.scale, tile_cfg=args.tile_cfg,
                               out=o, lse=lse)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr,
-          flush=True)
+    print(f"# settle {settled['ms']} ms ({settled['launches']} launches), warmup done "
+          f"({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
 
     # Timed region: K back-to-back launches on the current stream, bracketed by
     # synchronisation; HIP events on the same stream give the kernel's time.
@@ -288,6 +328,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": measured_traffic(w), "kernel_ms": round(ms_ev, 5)},
         "timing": timing,
+        "settle": settled,
         "device": device_info(),
     }
     out.update(extra)
@@ -320,6 +361,7 @@ def bench_merge(args, w, dev):
     def step():
         fa.flash_attn_merge(o_parts, lse_parts, out=o, lse=lse)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -346,6 +388,7 @@ def bench_merge(args, w, dev):
                      "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w),
                      "kernel_ms": round(ms_ev, 5)},
         "timing": timing,
+        "settle": settled,
         "device": device_info(),
     }
     if args.copy_calibration_mib:

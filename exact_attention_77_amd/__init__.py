@@ -144,6 +144,38 @@ def _layout_of(t) -> Layout:
     return Layout(B, H, N, d, t.stride(0), t.stride(1), t.stride(2))
 
 
+def _need(ok: bool, status: int, msg: str):
+    if not ok:
+        raise FlashAttnError(status, msg)
+
+
+def _check_buffer(t, name, dtype, shape, contiguous=True):
+    """A caller-supplied output or side input: exact dtype and shape (and
+    contiguity where the C ABI fixes the layout)."""
+    _need(t.dtype == dtype, 4, f"{name} must be {dtype}, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), 2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous:
+        _need(t.is_contiguous(), 3, f"{name} must be contiguous")
+
+
+def _on_gpu(*named):
+    """Every tensor the kernels will read or write must live on the current
+    GPU: a host pointer handed to a kernel would fault the device.  Checked
+    last, after the shape and dtype checks, so each of those is testable on a
+    host without a GPU."""
+    import torch
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        _need(t.is_cuda, 6, f"{name} is not on the GPU (device {t.device})")
+        if dev is None:
+            dev = t.device
+        _need(t.device == dev, 6, f"{name} is on {t.device}, the other tensors on {dev}")
+    _need(dev is None or dev.index == torch.cuda.current_device(), 6,
+          f"tensors are on {dev}, the current device is cuda:{torch.cuda.current_device()}")
+
+
 def _stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -175,10 +207,13 @@ def flash_attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
     if k.stride() != q.stride() or v.stride() != q.stride():
         raise FlashAttnError(3, "q, k, v must share strides")
     B, H, N, d = q.shape
+    if out is not None and (out.stride() != q.stride() or out.shape != q.shape or out.dtype != q.dtype):
+        raise FlashAttnError(3, "out must match q's shape, dtype and strides")
+    if lse is not None:
+        _check_buffer(lse, "lse", torch.float32, (B, H, N))
+    _on_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-    elif out.stride() != q.stride() or out.shape != q.shape or out.dtype != q.dtype:
-        raise FlashAttnError(3, "out must match q's shape, dtype and strides")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if scale is None:
@@ -199,8 +234,14 @@ def flash_attn_fp8_quantize(x, role: int, rotate: bool = False, signs=None):
     import torch
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise FlashAttnError(4, f"unsupported dtype {x.dtype}")
+    _need(x.dim() == 4, 2, "expected an [B, H, N, d] tensor")
+    _need(role in (ROLE_Q, ROLE_K, ROLE_V), 6, f"unknown role {role}")
     B, H, N, d = x.shape
     lay = _layout_of(x)
+    if rotate:
+        _need(signs is not None, 1, "rotate needs the +-1 signs")
+        _check_buffer(signs, "signs", torch.int8, (d,))
+    _on_gpu(("x", x), ("signs", signs if rotate else None))
     nbytes = flash_attn_fp8_buffer_bytes(lay, role)
     nsc = flash_attn_fp8_num_scales(lay, role)
     if role == ROLE_V:
@@ -223,18 +264,33 @@ def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = Fa
                        tile_cfg: int = 0, out=None, lse=None):
     """FP8 attention on the pre-pass outputs -> (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
     import torch
+    _need(q8.dim() == 4, 2, "q8 must be [B, H, N, d]")
     B, H, N, d = q8.shape
+    for t in (q8, k8, v8t):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise FlashAttnError(3, "fp8 inputs must be contiguous uint8 tensors")
+    npad = (N + 63) // 64 * 64
+    if tuple(k8.shape) != (B, H, N, d) or tuple(v8t.shape) != (B, H, d, npad):
+        raise FlashAttnError(2, f"k8 must match q8 and v8t must be [B, H, d, {npad}]")
+    lay = Layout(B, H, N, d, H * N * d, N * d, d)
+    for name, t, role in (("q_scale", q_scale, ROLE_Q), ("k_scale", k_scale, ROLE_K),
+                          ("v_scale", v_scale, ROLE_V)):
+        nsc = flash_attn_fp8_num_scales(lay, role)
+        _need(t.dtype == torch.float32 and t.is_contiguous(), 3, f"{name} must be contiguous float32")
+        _need(t.numel() == nsc, 2, f"{name} must hold {nsc} scales, got {t.numel()}")
+    if out is not None:
+        _check_buffer(out, "out", torch.bfloat16, (B, H, N, d), contiguous=False)
+        _need(d == 0 or out.stride(3) == 1, 3, "out must have a contiguous head_dim")
+    if lse is not None:
+        _check_buffer(lse, "lse", torch.float32, (B, H, N))
+    _on_gpu(("q8", q8), ("k8", k8), ("v8t", v8t), ("q_scale", q_scale), ("k_scale", k_scale),
+            ("v_scale", v_scale), ("out", out), ("lse", lse))
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d) if d else 1.0
-    for t in (q8, k8, v8t):
-        if t.dtype != torch.uint8 or not t.is_contiguous():
-            raise FlashAttnError(3, "fp8 inputs must be contiguous uint8 tensors")
-    if k8.shape != q8.shape or v8t.shape[:3] != (B, H, d):
-        raise FlashAttnError(2, "k8 must match q8; v8t must be [B, H, d, N_pad]")
     _check(load().flash_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
                                      q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
                                      out.data_ptr(), lse.data_ptr(), _layout_of(out),
@@ -268,13 +324,16 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | N
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise FlashAttnError(3, "lse must be a contiguous float32 [B, H, N] tensor")
     lay = _layout_of(q)
-    outs = []
     for t in (dq, dk, dv):
-        if t is None:
-            t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-        elif t.stride() != q.stride() or t.shape != q.shape or t.dtype != q.dtype:
+        if t is not None and (t.stride() != q.stride() or t.shape != q.shape or t.dtype != q.dtype):
             raise FlashAttnError(3, "gradient outputs must match q's shape, dtype and strides")
-        outs.append(t)
+    if workspace is not None:
+        _need(workspace.is_contiguous(), 3, "workspace must be contiguous")
+    _on_gpu(("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout), ("dq", dq),
+            ("dk", dk), ("dv", dv), ("workspace", workspace))
+    outs = [t if t is not None else
+            torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+            for t in (dq, dk, dv)]
     need = flash_attn_bwd_workspace_size(lay, DTYPE_BF16)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -301,11 +360,15 @@ def flash_attn_merge(o_parts, lse_parts, out=None, lse=None):
         raise FlashAttnError(3, "lse_parts must be contiguous float32")
     S, B, H, N, d = o_parts.shape
     lay = _layout_of(o_parts[0])
+    if out is not None and (out.stride() != o_parts.stride()[1:] or out.dtype != o_parts.dtype
+                            or tuple(out.shape) != (B, H, N, d)):
+        raise FlashAttnError(3, "out must have a part's shape, strides and dtype")
+    if lse is not None:
+        _check_buffer(lse, "lse", torch.float32, (B, H, N))
+    _on_gpu(("o_parts", o_parts), ("lse_parts", lse_parts), ("out", out), ("lse", lse))
     if out is None:
         out = torch.empty_strided((B, H, N, d), o_parts.stride()[1:], dtype=o_parts.dtype,
                                   device=o_parts.device)
-    elif out.stride() != o_parts.stride()[1:] or out.dtype != o_parts.dtype:
-        raise FlashAttnError(3, "out must have a part's strides and dtype")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
     dt = DTYPE_BF16 if o_parts.dtype == torch.bfloat16 else DTYPE_F32

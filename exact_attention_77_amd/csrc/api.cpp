@@ -44,15 +44,30 @@ flash_attn_status check_shape(const flash_attn_layout& L) {
     return FLASH_ATTN_OK;
 }
 
-// Strides must keep every row 16-byte aligned and must not make rows of
-// different (b, h, i) overlap in a way that aliases the output.
+// Strides must keep every row 16-byte aligned, and the map from (b, h, i, c)
+// to the element offset b*stride_b + h*stride_h + i*stride_s + c must be
+// one-to-one over the shape, so that no two workgroups ever write the same
+// output element.  Sorted by stride, each dimension of extent > 1 must step
+// past everything the smaller-stride dimensions span (the head_dim, stride 1,
+// is the innermost); this condition is sufficient for a one-to-one map.
 flash_attn_status check_strides(const flash_attn_layout& L, int64_t elt_bytes) {
     const int64_t vec = 16 / elt_bytes;
     if (L.stride_s < L.head_dim || L.stride_h < 0 || L.stride_b < 0) return FLASH_ATTN_ERR_LAYOUT;
     if (L.stride_s % vec || L.stride_h % vec || L.stride_b % vec) return FLASH_ATTN_ERR_LAYOUT;
-    // Distinct (b, h) must address distinct rows when there is more than one.
-    if (L.heads > 1 && L.stride_h < L.head_dim) return FLASH_ATTN_ERR_LAYOUT;
-    if (L.batch > 1 && L.stride_b < L.head_dim) return FLASH_ATTN_ERR_LAYOUT;
+    struct Dim { int64_t stride, extent; } dims[3] = {
+        {L.stride_s, L.seqlen}, {L.stride_h, L.heads}, {L.stride_b, L.batch}};
+    // insertion sort by stride (three entries)
+    for (int a = 1; a < 3; ++a)
+        for (int b = a; b > 0 && dims[b].stride < dims[b - 1].stride; --b) {
+            const Dim t = dims[b]; dims[b] = dims[b - 1]; dims[b - 1] = t;
+        }
+    int64_t span = L.head_dim;   // offsets 0 .. span-1 are covered so far
+    for (const Dim& d : dims) {
+        if (d.extent <= 1) continue;
+        if (d.stride < span) return FLASH_ATTN_ERR_LAYOUT;
+        // the shape limits keep this below 2^63
+        span += d.stride * (d.extent - 1);
+    }
     return FLASH_ATTN_OK;
 }
 

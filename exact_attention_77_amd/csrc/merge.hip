@@ -63,6 +63,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     auto weight = [&](int s) {
         return __builtin_amdgcn_exp2f((a.lse_parts[int64_t(s) * rows + row] - m) * kLog2e);
     };
+    // A part of weight 0 (LSE_s = -inf: no key; or a weight that underflows)
+    // adds nothing, whatever its O holds -- an empty shard's O may be 0/0.
+    auto add = [&](float w, const float (&x)[8]) {
+        total += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, w != 0.f ? x[e] : 0.f, acc[e]);
+    };
     if (m != -INFINITY) {
         // four parts' loads in flight before their products (the stream is
         // bound by how many bytes each lane keeps outstanding)
@@ -73,20 +80,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) load(s + u, x[u]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float w = weight(s + u);
-                total += w;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
-            }
+            for (int u = 0; u < U; ++u) add(weight(s + u), x[u]);
         }
         for (; s < a.S; ++s) {
             float x[8];
             load(s, x);
-            const float w = weight(s);
-            total += w;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+            add(weight(s), x);
         }
     }
     // no key in any part: O = 0, LSE = -inf

@@ -30,6 +30,11 @@
  *    Base pointers must be 16-byte aligned and the strides multiples of
  *    16 bytes' worth of elements (8 for bf16, 4 for f32, 16 for fp8).
  *  - LSE is always a contiguous fp32 [B, H, N] array.
+ *  - Inputs must be finite.  A NaN or infinite element of Q, K or V leaves the
+ *    outputs of the rows that use it (and possibly of other rows whose key
+ *    tile contains it) unspecified: the attention kernels are compiled
+ *    assuming no NaN operands, which lets a row maximum be one v_max3 per two
+ *    scores.  Rows that never load that tile are unaffected.
  *  - Supported v1: head_dim 64 or 128; seqlen_q == seqlen_k == seqlen.
  *    A zero batch, heads or seqlen is a valid empty call (returns OK, no work;
  *    pointers may then be NULL).

@@ -50,12 +50,34 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+_NATIVE = os.path.join(_HERE, "liboracle_native.so")
+_use_native = False
+
+
+def use_native_build() -> str:
+    """Compile oracle.c for the host it runs on (gcc -O3 -march=native, FMA
+    contraction off so the rounding is that of the plain build, no fast-math)
+    and make this process load that build.  For timing the oracle as a CPU
+    baseline; must be called before the first oracle call."""
+    global _use_native
+    if _lib is not None:
+        raise RuntimeError("the oracle library is already loaded")
+    tmp = _NATIVE + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O3", "-march=native", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                           "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _NATIVE)
+    _use_native = True
+    return _NATIVE
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
             if _LIB_OVERRIDE:
                 lib = ctypes.CDLL(_LIB_OVERRIDE)
+            elif _use_native:
+                lib = ctypes.CDLL(_NATIVE)
             else:
                 build()
                 lib = ctypes.CDLL(_LIB)
@@ -234,8 +256,9 @@ def merge(o_parts, lse_parts):
 
     o_parts: [S, ..., d] normalised outputs; lse_parts: [S, ...] natural-log LSE.
     Returns (o, lse) with LSE = ln sum_s exp(LSE_s) and
-    o = sum_s exp(LSE_s - LSE) o_s.  A row whose parts all have LSE = -inf
-    (no key at all) gets o = 0 and LSE = -inf.
+    o = sum_s exp(LSE_s - LSE) o_s.  A part with LSE_s = -inf adds nothing
+    (even if its o_s is not finite); a row whose parts all have LSE = -inf (no
+    key at all) gets o = 0 and LSE = -inf.
     """
     o = _f64(o_parts)
     lse = _f64(lse_parts)
@@ -247,4 +270,52 @@ def merge(o_parts, lse_parts):
     total = w.sum(axis=0)
     lse_out = np.where(alive, m0 + np.log(np.where(alive, total, 1.0)), -np.inf)
     frac = np.where(alive, w / np.where(alive, total, 1.0), 0.0)
-    return (frac[..., None] * o).sum(axis=0), lse_out
+    # a part of weight 0 contributes nothing, whatever its O holds (an empty
+    # part's O may be undefined, e.g. 0/0)
+    terms = np.where(frac[..., None] > 0, frac[..., None] * np.where(frac[..., None] > 0, o, 0.0), 0.0)
+    return terms.sum(axis=0), lse_out
+
+
+def bf16_round(x) -> np.ndarray:
+    """x rounded to the nearest bfloat16 value (8 significant bits, ties to
+    even), returned as fp64.  Written from the format: x = m * 2^e with
+    m in [0.5, 1); m * 2^8 is rounded to the nearest integer, ties to even
+    (numpy's rint), and scaled back.  Normal range only (|x| >= 2^-126 or 0),
+    which covers every value it is used on here."""
+    x = _f64(x)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def attn_bwd_bf16_baseline(q, k, v, dout, causal: bool = False, scale: float | None = None):
+    """Comparison baseline for the bf16 backward: standard (non-fused)
+    attention whose materialised intermediates are stored in bf16, in the
+    comparison style of the FP16 rows of "FlashAttention-3: ...", 数値誤差
+    ("standard attention" against an fp64 reference).  Per (b, h), in fp64:
+    P = softmax(scale Q K^T) (masked), O = bf16(P V);
+    dV = bf16(P)^T dO;  dP = dO V^T;  D = rowsum(dO o O);
+    dS = bf16(P o (dP - D));  dQ = scale dS K;  dK = scale dS^T Q;
+    each gradient rounded to bf16 at the end.  The roundings are the ones a
+    bf16 implementation cannot avoid (P and dS enter products as bf16, O and
+    the gradients are stored as bf16); everything else is exact fp64."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = (np.empty_like(q) for _ in range(3))
+    mask = np.tril(np.ones((N, N), dtype=bool)) if causal else None
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                s = np.where(mask, s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = bf16_round(p @ v[b, h])
+            dv[b, h] = bf16_round(bf16_round(p).T @ dout[b, h])
+            dp = dout[b, h] @ v[b, h].T
+            D = np.sum(dout[b, h] * o, axis=1, keepdims=True)
+            ds = bf16_round(p * (dp - D))
+            dq[b, h] = bf16_round(scale * (ds @ k[b, h]))
+            dk[b, h] = bf16_round(scale * (ds.T @ q[b, h]))
+    return dq, dk, dv

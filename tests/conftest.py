@@ -26,3 +26,25 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+# Parity margins of the full-size workloads, printed after the test summary
+# so that they appear at the end of the run's output even when pytest
+# captures each test's own output.
+_MARGINS = []
+
+
+@pytest.fixture
+def margin():
+    """margin(line): record one line for the end-of-run margin summary."""
+    def add(line: str):
+        _MARGINS.append(line)
+        print(line, flush=True)
+    return add
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    if _MARGINS:
+        terminalreporter.write_sep("-", "parity margins (full-size workloads)")
+        for line in _MARGINS:
+            terminalreporter.write_line(line)

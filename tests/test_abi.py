@@ -87,6 +87,29 @@ def test_bad_strides(lay):
     assert fwd(lay=lay) == 3
 
 
+@pytest.mark.parametrize("lay", [
+    # rows of different (b, h, i) that share memory: two workgroups would write
+    # the same output element
+    fa.Layout(1, 2, 2, 64, 128, 64, 64),          # stride_h == stride_s
+    fa.Layout(1, 2, 4, 64, 1024, 128, 64),        # head 1 starts inside head 0's rows
+    fa.Layout(2, 2, 4, 64, 128, 256, 64),         # batch 1 starts inside head 0 of batch 0
+    fa.Layout(2, 1, 8, 64, 0, 512, 64),           # batch stride 0 with two batches
+    fa.Layout(1, 3, 2, 128, 0, 192, 128)])        # head 1 starts inside head 0's second row
+def test_overlapping_rows_rejected(lay):
+    assert fwd(lay=lay) == 3
+    assert fa.load().flash_attn_bwd(P, P, P, P, P, P, P, P, P, lay, fa.DTYPE_BF16, 0, 0.125,
+                                    P, 1 << 30, None) == 3
+
+
+@pytest.mark.parametrize("lay", [
+    fa.Layout(2, 3, 5, 64, 3 * 5 * 64, 5 * 64, 64),   # [B, H, N, d]
+    fa.Layout(2, 3, 5, 64, 5 * 3 * 64, 64, 3 * 64),   # [B, N, H, d]
+    fa.Layout(1, 4, 1, 128, 0, 128, 128),            # one row: its stride is irrelevant
+    fa.Layout(3, 1, 7, 64, 7 * 64 + 64, 0, 64)])     # one head, padded batches
+def test_one_to_one_layouts_accepted(lay):
+    assert fwd(lay=lay, q=None) == 1   # passes every layout check, then reports the NULL q
+
+
 def test_misaligned_pointers():
     assert fwd(q=P + 2) == 3
     assert fwd(o=P + 8) == 3

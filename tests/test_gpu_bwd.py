@@ -8,7 +8,10 @@ Tolerance (no figure on the pages; derived from the arithmetic): P and dS
 enter the matrix products as bf16 (relative rounding 2^-9), O reaches the
 row statistic D as bf16, and every product accumulates in fp32.  Per tensor
 we require  max|err| <= 2e-2 * max(1, max|ref|)  and an RMS error at most
-1e-2 * max(reference RMS, 1e-2).
+1e-2 * max(reference RMS, 1e-2).  Beside it, the RMS error must be within
+twice that of a bf16 standard-attention backward computed on the CPU (the
+oracle's baseline with the same unavoidable bf16 roundings).  Every shape,
+the full-size workload included, is compared on every row.
 """
 import numpy as np
 import pytest
@@ -50,23 +53,35 @@ def _fwd_bwd(dev, causal, workspace=None):
     return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
 
 
-def _compare(name, got, ref):
+def _compare(name, got, ref, report=print):
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), name
     err = np.abs(got - ref)
     bound = ABS_TOL * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
     rms_ref = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     rms_err = float(np.sqrt(np.mean(err ** 2))) if ref.size else 0.0
-    print(f"{name}: max|err|={err.max() if err.size else 0:.3e} (bound {bound:.3e}) "
-          f"rms err/ref={rms_err / max(rms_ref, 1e-30):.3e}", flush=True)
+    report(f"{name}: max|err|={err.max() if err.size else 0:.3e} (bound {bound:.3e}) "
+           f"rms err/ref={rms_err / max(rms_ref, 1e-30):.3e}")
     assert err.size == 0 or float(err.max()) <= bound, name
     assert rms_err <= RMS_TOL * max(rms_ref, RMS_FLOOR), name
 
 
-def _check_full(grads, ref, causal):
-    rq, rk, rv = oracle.attn_bwd(*ref, causal=causal)
-    for name, g, r in zip(("dQ", "dK", "dV"), grads, (rq, rk, rv)):
-        _compare(name, g, r)
+def _check_full(grads, ref, causal, report=print):
+    """Against the exact gradient (bounds above), and against the baseline a
+    bf16 standard-attention backward reaches (P and dS enter the products as
+    bf16, O and the gradients are stored as bf16): the RMS error must stay
+    within twice the baseline's (the comparison style of the FP16 rows of
+    "FlashAttention-3: ...", 数値誤差)."""
+    exact = oracle.attn_bwd(*ref, causal=causal)
+    base = oracle.attn_bwd_bf16_baseline(*ref, causal=causal)
+    for name, g, r, b in zip(("dQ", "dK", "dV"), grads, exact, base):
+        _compare(name, g, r, report)
+        rms_ref = float(np.sqrt(np.mean(r ** 2))) if r.size else 0.0
+        rms_gpu = float(np.sqrt(np.mean((g - r) ** 2))) if r.size else 0.0
+        rms_base = float(np.sqrt(np.mean((b - r) ** 2))) if r.size else 0.0
+        report(f"{name}: rms err {rms_gpu:.3e} vs bf16 standard attention {rms_base:.3e} "
+               f"(ratio {rms_gpu / max(rms_base, 1e-30):.2f}, bound 2)")
+        assert rms_gpu <= 2.0 * rms_base + 1e-4 * max(rms_ref, RMS_FLOOR), name
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -105,21 +120,12 @@ def test_bwd_dirty_workspace_and_repeat():
     _check_full(a, ref, True)
 
 
-def test_bwd_full_size_sampled():
-    """Backward workload at its full size (B=2, H=16, N=4096, d=128, causal),
-    compared on sampled rows of the first and last head (the oracle's row
-    statistics cost O(N^2 d) per touched head)."""
+def test_bwd_full_size_all_rows(margin):
+    """Backward workload at its full size (B=2, H=16, N=4096, d=128, causal):
+    every row of dQ, dK and dV of every head against the oracle, and against
+    the bf16 standard-attention baseline."""
     w = WORKLOADS["bf16_bwd_causal_n4096_d128"]
     print(f"bwd full size {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
     dev, ref = _inputs(w.B, w.H, w.N, w.d, w.seed)
     grads = _fwd_bwd(dev, w.causal)
-    g = np.random.Generator(np.random.PCG64(w.seed + 17))
-    last = (w.B * w.H - 1) * w.N
-    rows = np.unique(np.concatenate([
-        np.array([0, 1, w.N - 1, last, last + w.N - 1], np.int64),
-        g.integers(0, w.N, 40), last + g.integers(0, w.N, 40)]).astype(np.int64))
-    rq, rk, rv = oracle.attn_bwd(*ref, causal=w.causal, qrows=rows, krows=rows)
-    d = w.d
-    for name, full, r in zip(("dQ", "dK", "dV"), grads, (rq, rk, rv)):
-        assert np.all(np.isfinite(full)), name
-        _compare(name, full.reshape(-1, d)[rows], r)
+    _check_full(grads, ref, w.causal, lambda line: margin(f"bwd {w.name} all rows {line}"))

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+from synth_inputs import normal_qkv
 
 
 def _rand(seed, shape):
@@ -77,3 +78,47 @@ def test_row_subset_matches_full(causal):
     assert np.max(np.abs(sq - dq.reshape(-1, 8)[qr])) <= 1e-14
     assert np.max(np.abs(sk - dk.reshape(-1, 8)[kr])) <= 1e-14
     assert np.max(np.abs(sv - dv.reshape(-1, 8)[kr])) <= 1e-14
+
+
+# ---- bf16 rounding and the bf16 standard-attention backward baseline ----
+
+def test_bf16_round_matches_torch():
+    import torch
+    g = np.random.default_rng(40)
+    x = (g.standard_normal(50000) * 10.0 ** g.integers(-20, 20, 50000)).astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_round(x), want)
+    # exact midpoints between neighbouring bf16 values go to the even one
+    lo = torch.from_numpy(x[:2000].astype(np.float32)).to(torch.bfloat16)
+    lo_bits = lo.view(torch.int16).numpy().astype(np.int64)
+    hi = torch.from_numpy((lo_bits + 1).astype(np.int16)).view(torch.bfloat16)
+    a, b = lo.to(torch.float64).numpy(), hi.to(torch.float64).numpy()
+    fin = np.isfinite(a) & np.isfinite(b) & (np.sign(a) == np.sign(b)) & (a != 0)
+    mid = 0.5 * (a + b)[fin]
+    got = oracle.bf16_round(mid)
+    even = np.where(lo_bits[fin] % 2 == 0, a[fin], b[fin])
+    assert np.array_equal(got, even)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_baseline_single_key_is_exact(causal):
+    # one key: P = 1, O = v_0, dS = dO . (v_0 - O) = 0 for bf16 inputs, so
+    # dQ = dK = 0 and dV = dO exactly
+    import torch
+    g = np.random.default_rng(41)
+    x = [torch.from_numpy(g.standard_normal((2, 3, 1, 8)).astype(np.float32)).to(torch.bfloat16)
+         .to(torch.float64).numpy() for _ in range(4)]
+    dq, dk, dv = oracle.attn_bwd_bf16_baseline(*x, causal=causal)
+    assert np.all(dq == 0) and np.all(dk == 0) and np.array_equal(dv, x[3])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_baseline_is_near_the_exact_gradient(causal):
+    """Its error against the exact gradient is that of a few bf16 roundings:
+    relative RMS between 1e-4 (some rounding happened) and 1e-2."""
+    q, k, v, do = (x.astype(np.float64) for x in normal_qkv(1, 2, 70, 16, 42, with_dout=True))
+    exact = oracle.attn_bwd(q, k, v, do, causal=causal)
+    base = oracle.attn_bwd_bf16_baseline(q, k, v, do, causal=causal)
+    for e, b in zip(exact, base):
+        rel = np.sqrt(np.mean((b - e) ** 2)) / np.sqrt(np.mean(e ** 2))
+        assert 1e-4 < rel < 1e-2, rel

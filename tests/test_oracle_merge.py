@@ -64,3 +64,13 @@ def test_extreme_lse_and_empty_parts():
     # no keys at all: O = 0, LSE = -inf
     mo, ml = oracle.merge(o, np.full((2, 1), -np.inf))
     assert np.all(mo == 0.0) and ml[0] == -np.inf
+
+
+def test_empty_part_with_undefined_output_adds_nothing():
+    # an empty shard's normalised output is 0/0: its weight is 0 and so is its
+    # contribution, NaN or not
+    o = np.stack([np.full((2, 4), 2.0), np.full((2, 4), np.nan), np.full((2, 4), np.inf)])
+    lse = np.array([[0.5, -1.0], [-np.inf, -np.inf], [-np.inf, 3.0]])
+    mo, ml = oracle.merge(o, lse)
+    assert np.array_equal(mo[0], np.full(4, 2.0)) and ml[0] == 0.5
+    assert np.all(np.isinf(mo[1]))          # row 1: the third part carries weight
