@@ -8,6 +8,7 @@ for device memory and the current stream.  The functions carry the C names:
     flash_attn_fp8_quantize(x, role, rotate=False, signs=None) -> (x_fp8, scales)
     flash_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale) -> (o_bf16, lse)
     flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+    flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal, scale)
     flash_attn_merge(o_parts, lse_parts) -> (o, lse)
 
 If the shared library is missing this module raises on first use: there is no
@@ -23,7 +24,7 @@ import threading
 __all__ = [
     "FlashAttnError", "lib_path", "load", "flash_attn_fwd", "flash_attn_fp8_quantize",
     "flash_attn_fwd_fp8", "flash_attn_fp8_buffer_bytes", "flash_attn_fp8_num_scales",
-    "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_merge",
+    "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_bwd_noalloc", "flash_attn_merge",
     "flash_attn_status_str", "flash_attn_last_error", "flash_attn_abi_version", "Layout",
     "FwdOpts", "STATUS", "DTYPE_F32", "DTYPE_BF16", "DTYPE_FP8_E4M3", "ROLE_Q", "ROLE_K",
     "ROLE_V", "EXPORTED_SYMBOLS",
@@ -45,8 +46,8 @@ STATUS = {
 EXPORTED_SYMBOLS = (
     "flash_attn_fwd", "flash_attn_fp8_quantize", "flash_attn_fp8_buffer_bytes",
     "flash_attn_fp8_num_scales", "flash_attn_fwd_fp8", "flash_attn_bwd",
-    "flash_attn_bwd_workspace_size", "flash_attn_merge", "flash_attn_status_str",
-    "flash_attn_last_error", "flash_attn_abi_version",
+    "flash_attn_bwd_workspace_size", "flash_attn_bwd_noalloc", "flash_attn_merge",
+    "flash_attn_status_str", "flash_attn_last_error", "flash_attn_abi_version",
 )
 
 
@@ -97,6 +98,8 @@ def load():
         lib.flash_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, Layout, I, I, F, P,
                                        ctypes.c_size_t, P]
         lib.flash_attn_bwd.restype = I
+        lib.flash_attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, Layout, I, I, F, P]
+        lib.flash_attn_bwd_noalloc.restype = I
         lib.flash_attn_bwd_workspace_size.argtypes = [Layout, I]
         lib.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.flash_attn_merge.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P, Layout, I, P]
@@ -345,6 +348,34 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | N
                                  int(bool(causal)), float(scale), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream()))
     return tuple(outs)
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool = False,
+                           scale: float | None = None):
+    """The backward into caller-supplied dq, dk, dv without any device
+    allocation: the per-row workspace is the library's fixed device array
+    (B * H * N <= 2^21 rows).  Same arguments and result as flash_attn_bwd."""
+    import torch
+    ts = (q, k, v, o, dout, dq, dk, dv)
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise FlashAttnError(4, "the backward takes bfloat16 tensors")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise FlashAttnError(2, "q, k, v, o, dout, dq, dk, dv must share a [B, H, N, d] shape")
+    if any(t.stride() != q.stride() for t in ts):
+        raise FlashAttnError(3, "q, k, v, o, dout, dq, dk, dv must share strides")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise FlashAttnError(3, "lse must be a contiguous float32 [B, H, N] tensor")
+    lay = _layout_of(q)
+    _on_gpu(("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout), ("dq", dq),
+            ("dk", dk), ("dv", dv))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d else 1.0
+    _check(load().flash_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                         dk.data_ptr(), dv.data_ptr(), lay, DTYPE_BF16,
+                                         int(bool(causal)), float(scale), _stream()))
+    return dq, dk, dv
 
 
 def flash_attn_merge(o_parts, lse_parts, out=None, lse=None):

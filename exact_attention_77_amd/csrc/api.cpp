@@ -224,11 +224,18 @@ size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype 
         fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen));
 }
 
-flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                 flash_attn_layout layout, flash_attn_dtype dtype, int causal,
-                                 float scale, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by both backward entry points.  With
+// from_scratch the workspace is the library's fixed device array instead of
+// the caller's (no allocation either way).
+flash_attn_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           flash_attn_layout layout, flash_attn_dtype dtype, int causal,
+                           float scale, void* workspace, size_t workspace_bytes,
+                           bool from_scratch, void* stream) {
     flash_attn_status st = check_shape(layout);
     if (st != FLASH_ATTN_OK) return st;
     if (dtype == FLASH_ATTN_F32) return FLASH_ATTN_ERR_UNSUPPORTED;
@@ -243,6 +250,12 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
         (reinterpret_cast<uintptr_t>(lse) & 3u))
         return FLASH_ATTN_ERR_LAYOUT;
     const int64_t need = fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen);
+    if (from_scratch) {
+        if (need > fa::kScratchBytes) return FLASH_ATTN_ERR_WORKSPACE;
+        const int err = fa::scratch_buffer(&workspace);
+        if (err) return hip_status(err);
+        workspace_bytes = static_cast<size_t>(fa::kScratchBytes);
+    }
     if (!workspace || workspace_bytes < static_cast<size_t>(need) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return FLASH_ATTN_ERR_WORKSPACE;
@@ -262,6 +275,28 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
     a.ws_lse2 = reinterpret_cast<float*>(ws);
     a.ws_nd = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows));
     return hip_status(fa::launch_bwd_bf16(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                 flash_attn_layout layout, flash_attn_dtype dtype, int causal,
+                                 float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, layout, dtype, causal, scale, workspace,
+                    workspace_bytes, false, stream);
+}
+
+flash_attn_status flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                         const void* o, const float* lse, const void* dout,
+                                         void* dq, void* dk, void* dv, flash_attn_layout layout,
+                                         flash_attn_dtype dtype, int causal, float scale,
+                                         void* stream) {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, layout, dtype, causal, scale, nullptr, 0,
+                    true, stream);
 }
 
 flash_attn_status flash_attn_merge(const void* o_parts, const float* lse_parts, int64_t n_parts,

@@ -89,6 +89,13 @@ inline int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
     return 2 * bwd_ws_part(B * H * N);
 }
 
+// Fixed device scratch buffer (scratch.hip) for the allocation-free backward:
+// its size bounds B * H * N at 2^21 rows (two fp32 values per row).
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+// Device address of the scratch array on the current device (looked up once
+// per device); returns a hipError_t value.
+int scratch_buffer(void** ptr);
+
 // Launchers: return a hipError_t value (0 = success).
 int launch_fwd_bf16(const FwdArgs& a, void* stream);
 int launch_fwd_f32(const FwdArgs& a, void* stream);

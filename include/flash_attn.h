@@ -206,6 +206,28 @@ flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, co
 size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype dtype);
 
 /*
+ * flash_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not allocate, harnesses that forbid hipMalloc.  The two fp32 values
+ * per query row that flash_attn_bwd keeps in the caller's workspace live in
+ * a fixed device array of the library instead (16 MiB per GPU, held until
+ * the process ends; its address is looked up once per device, with that
+ * device current).  The call allocates nothing.
+ *   Arguments, results and errors: as flash_attn_bwd (the result is the same,
+ *   bit for bit); the stream must belong to the current device.
+ *   Limit: batch * heads * seqlen <= 2^21 rows; larger shapes return
+ *   FLASH_ATTN_ERR_WORKSPACE (use flash_attn_bwd with a workspace).
+ *   Every call on one GPU shares the array: calls that overlap on one GPU
+ *   (several streams or host threads at once) race and must be serialised by
+ *   the caller.
+ */
+flash_attn_status flash_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                         const void* o, const float* lse, const void* dout,
+                                         void* dq, void* dk, void* dv,
+                                         flash_attn_layout layout, flash_attn_dtype dtype,
+                                         int causal, float scale, void* stream);
+
+/*
  * Merge of attention results over disjoint key sets (the combine step of
  * attention sharded along the sequence).  Part s holds, for every row, the
  * normalised output O_s over its keys and the natural-log LSE_s of its scaled

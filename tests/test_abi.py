@@ -229,3 +229,18 @@ def test_c_consumer_compiles(tmp_path):
     out = str(tmp_path / "abi_consumer")
     subprocess.run(mod.command(out), check=True)
     assert os.path.getsize(out) > 0
+
+
+def bwd_noalloc(lay, q=P, lse=P, dtype=fa.DTYPE_BF16):
+    return fa.load().flash_attn_bwd_noalloc(q, P, P, P, lse, P, P, P, P, lay, dtype, 0, 0.125, None)
+
+
+def test_bwd_noalloc_validation():
+    # the fixed scratch array holds two fp32 values for at most 2^21 rows
+    big = fa.Layout(2, 16, 65537, 64, 16 * 65537 * 64, 65537 * 64, 64)
+    assert bwd_noalloc(big) == 7                      # ERR_WORKSPACE, before any HIP call
+    assert bwd_noalloc(_lay(N=0)) == 0
+    assert bwd_noalloc(_lay(), q=None) == 1
+    assert bwd_noalloc(_lay(), dtype=fa.DTYPE_F32) == 5
+    assert bwd_noalloc(_lay(ss=60)) == 3
+    assert bwd_noalloc(_lay(), lse=P + 2) == 3
