@@ -240,9 +240,10 @@ def main():
         pp_ms, f8 = timed_rounds(10, True)
         extra["prepass_host_bound_ms"] = round(timed_rounds(10, False)[0], 5)   # launched one by one
         # algorithmic bytes of the three pre-pass calls: fp32 Q, K, V read once,
-        # e4m3 codes written (V transposed and padded to 64 keys), fp32 scales
+        # e4m3 codes written (Q: the code and its residual term; V transposed
+        # and padded to 64 keys), fp32 scales
         elems, npad = w.B * w.H * w.N * w.d, (w.N + 63) // 64 * 64
-        pp_bytes = (3 * elems * 4 + 2 * elems + w.B * w.H * w.d * npad
+        pp_bytes = (3 * elems * 4 + 3 * elems + w.B * w.H * w.d * npad
                     + 4 * w.B * w.H * (2 * ((w.N + 31) // 32) + npad // 64))
         extra["prepass_ms"] = round(pp_ms, 5)
         extra["prepass_roofline"] = {"bound": "hbm", "achieved": round(pp_bytes / (pp_ms * 1e-3) / 1e9, 1),
@@ -304,6 +305,22 @@ def main():
     kernel_tflops = w.flops / (ms_ev * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     timing = launch_stats(step, stream, dev, min(50, args.steps))
+    if w.dtype == "fp8":
+        # the faster form that uses Q's first e4m3 term only (opts.fp8_q_terms = 1)
+        def step1():
+            fa.flash_attn_fwd_fp8(*f8, causal=w.causal, scale=w.scale, tile_cfg=args.tile_cfg,
+                                  out=o, lse=lse, q_terms=1)
+        for _ in range(max(args.warmup, 20)):
+            step1()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step1()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms1 = e0.elapsed_time(e1) / args.steps
+        extra["one_term_q"] = {"ms_per_step": round(ms1, 5), "tflops": round(w.flops / (ms1 * 1e-3) / 1e12, 2)}
 
     out = {
         "metric": METRIC if w.name == "bf16_causal_n8192_d128" else

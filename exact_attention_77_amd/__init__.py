@@ -67,7 +67,7 @@ class Layout(ctypes.Structure):
 
 class FwdOpts(ctypes.Structure):
     _fields_ = [("tau_log2", ctypes.c_float), ("tile_cfg", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("fp8_q_terms", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -184,10 +184,11 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _opts(tau_log2, tile_cfg):
-    if tau_log2 is None and not tile_cfg:
+def _opts(tau_log2, tile_cfg, q_terms=0):
+    if tau_log2 is None and not tile_cfg and not q_terms:
         return None
-    return ctypes.byref(FwdOpts(-1.0 if tau_log2 is None else float(tau_log2), int(tile_cfg), 0))
+    return ctypes.byref(FwdOpts(-1.0 if tau_log2 is None else float(tau_log2), int(tile_cfg),
+                                int(q_terms)))
 
 
 def flash_attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
@@ -231,8 +232,9 @@ def flash_attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
 def flash_attn_fp8_quantize(x, role: int, rotate: bool = False, signs=None):
     """Rotate (optionally, Q/K) and block-quantise x [B, H, N, d] (f32/bf16) to e4m3.
 
-    Returns (x_fp8, scales): uint8 [B, H, N, d] for Q/K, the transposed
-    [B, H, d, N_pad] for V; fp32 scales [B, H, n_blocks].
+    Returns (x_fp8, scales): uint8 [2, B, H, N, d] for Q (the code and its
+    residual term), [B, H, N, d] for K, the transposed [B, H, d, N_pad] for V;
+    fp32 scales [B, H, n_blocks].
     """
     import torch
     if x.dtype not in (torch.float32, torch.bfloat16):
@@ -250,6 +252,8 @@ def flash_attn_fp8_quantize(x, role: int, rotate: bool = False, signs=None):
     if role == ROLE_V:
         npad = (N + 63) // 64 * 64
         out = torch.empty((B, H, d, npad), dtype=torch.uint8, device=x.device)
+    elif role == ROLE_Q:   # the code and its residual term
+        out = torch.empty((2, B, H, N, d), dtype=torch.uint8, device=x.device)
     else:
         out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
     assert out.numel() == nbytes
@@ -264,11 +268,12 @@ def flash_attn_fp8_quantize(x, role: int, rotate: bool = False, signs=None):
 
 def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False,
                        scale: float | None = None, tau_log2: float | None = None,
-                       tile_cfg: int = 0, out=None, lse=None):
-    """FP8 attention on the pre-pass outputs -> (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
+                       tile_cfg: int = 0, out=None, lse=None, q_terms: int = 0):
+    """FP8 attention on the pre-pass outputs (q8 [2, B, H, N, d], k8 [B, H, N, d],
+    v8t [B, H, d, N_pad] uint8 and their scales) -> (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
     import torch
-    _need(q8.dim() == 4, 2, "q8 must be [B, H, N, d]")
-    B, H, N, d = q8.shape
+    _need(q8.dim() == 5 and q8.shape[0] == 2, 2, "q8 must be [2, B, H, N, d] (code, residual term)")
+    _, B, H, N, d = q8.shape
     for t in (q8, k8, v8t):
         if t.dtype != torch.uint8 or not t.is_contiguous():
             raise FlashAttnError(3, "fp8 inputs must be contiguous uint8 tensors")
@@ -297,8 +302,8 @@ def flash_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = Fa
     _check(load().flash_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
                                      q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
                                      out.data_ptr(), lse.data_ptr(), _layout_of(out),
-                                     int(bool(causal)), float(scale), _opts(tau_log2, tile_cfg),
-                                     _stream()))
+                                     int(bool(causal)), float(scale),
+                                     _opts(tau_log2, tile_cfg, q_terms), _stream()))
     return out, lse
 
 

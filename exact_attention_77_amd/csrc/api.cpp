@@ -71,11 +71,14 @@ flash_attn_status check_strides(const flash_attn_layout& L, int64_t elt_bytes) {
     return FLASH_ATTN_OK;
 }
 
-flash_attn_status check_opts(const flash_attn_fwd_opts* opts, float* tau, int* tile_cfg) {
+flash_attn_status check_opts(const flash_attn_fwd_opts* opts, float* tau, int* tile_cfg,
+                             int* q_terms = nullptr) {
     *tau = 8.0f;
     *tile_cfg = 0;
+    if (q_terms) *q_terms = 2;
     if (!opts) return FLASH_ATTN_OK;
-    if (opts->reserved != 0) return FLASH_ATTN_ERR_ARG;
+    if (opts->fp8_q_terms < 0 || opts->fp8_q_terms > 2) return FLASH_ATTN_ERR_ARG;
+    if (q_terms && opts->fp8_q_terms != 0) *q_terms = opts->fp8_q_terms;
     if (isnan(opts->tau_log2)) return FLASH_ATTN_ERR_ARG;
     if (opts->tau_log2 >= 0.0f) {
         if (!(opts->tau_log2 <= 64.0f)) return FLASH_ATTN_ERR_ARG;
@@ -167,7 +170,8 @@ size_t flash_attn_fp8_buffer_bytes(flash_attn_layout layout, flash_attn_fp8_role
     if (layout.batch < 0 || layout.heads < 0 || layout.seqlen < 0 || layout.head_dim < 0) return 0;
     if (role != FLASH_ATTN_FP8_Q && role != FLASH_ATTN_FP8_K && role != FLASH_ATTN_FP8_V) return 0;
     const int64_t rows = (role == FLASH_ATTN_FP8_V) ? fa::fp8_npad(layout.seqlen) : layout.seqlen;
-    return static_cast<size_t>(layout.batch * layout.heads * rows * layout.head_dim);
+    const int64_t planes = (role == FLASH_ATTN_FP8_Q) ? 2 : 1;   // Q: the code and its residual term
+    return static_cast<size_t>(planes * layout.batch * layout.heads * rows * layout.head_dim);
 }
 
 int64_t flash_attn_fp8_num_scales(flash_attn_layout layout, flash_attn_fp8_role role) {
@@ -192,8 +196,8 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
     if (causal != 0 && causal != 1) return FLASH_ATTN_ERR_ARG;
     if ((st = check_scale(scale)) != FLASH_ATTN_OK) return st;
     float tau;
-    int tile_cfg;
-    if ((st = check_opts(opts, &tau, &tile_cfg)) != FLASH_ATTN_OK) return st;
+    int tile_cfg, q_terms;
+    if ((st = check_opts(opts, &tau, &tile_cfg, &q_terms)) != FLASH_ATTN_OK) return st;
     if (is_empty(o_layout)) return FLASH_ATTN_OK;
     if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o || !lse)
         return FLASH_ATTN_ERR_NULL;
@@ -214,6 +218,7 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
     a.tau = fminf(tau, 2.5f);  // 64 * 2^tau must stay below 448
     a.causal = causal;
     a.tile_cfg = tile_cfg;
+    a.q_terms = q_terms;
     return hip_status(fa::launch_fwd_fp8(a, stream));
 }
 

@@ -41,6 +41,7 @@ namespace fa {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
@@ -184,6 +185,34 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantArgs a) {
             op[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
             op[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
         }
+        if (a.role == 0) {
+            // Q: a second e4m3 term for the rounding residual, in units of
+            // 2^-4 of the scaled value: lo = e4m3(16 (y - hi)), |16 (y - hi)|
+            // <= 256 (half an e4m3 step is at most 2^-4 |y| and |y| <= 448),
+            // so Q = scale (hi + lo / 16) to about 2^-8 relative.
+            uint32_t wl[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // decoded hi values: bytes 0-1 and 2-3 of the word
+                const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wq[i]), false);
+                const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wq[i]), true);
+                const float hv[4] = {h01[0], h01[1], h23[0], h23[1]};
+                float r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = fminf(fmaxf(x[4 * i + e] * rcp, -448.f), 448.f);
+                    r[e] = (y - hv[e]) * 16.f;
+                }
+                const int lo = cvt2<false>(r[0], r[1], 0);
+                wl[i] = static_cast<uint32_t>(cvt2<true>(r[2], r[3], lo));
+            }
+            if (row < a.N) {   // the second plane follows the first: [2][B, H, N, D]
+                uint4* lp = reinterpret_cast<uint4*>(a.out + int64_t(a.B) * a.H * a.N * D +
+                                                     (int64_t(bh) * a.N + row) * D + 32 * c);
+                lp[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+                lp[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+            }
+        }
         return;
     }
     // V: [D][RWG] bytes through LDS (rows past N hold zero codes), then rows of
@@ -232,6 +261,19 @@ __device__ __forceinline__ int krow8(int rho, int st) {
     return 32 * ((rho >> 2) & 1) + 16 * st + 4 * (rho >> 3) + (rho & 3);
 }
 
+// A operand of the row-sum product v_mfma_scale_f32_16x16x128_f8f6f4(A, P, 0):
+// fed as its B operand, the probabilities of lane l (query l % 32, keys of
+// lane half l / 32) are column l % 16 of K-block l / 16 (32 values each).  A
+// row m holds e4m3 ones (0x38) in the K-blocks whose parity is that of m / 4
+// when m % 4 == 0, zeros elsewhere, so output row 4g, column c -- register 0
+// of lane 16g + c -- sums both lane halves of query (16g + c) % 32: every lane
+// receives its own query's row sum over the 64-key tile.
+__device__ __forceinline__ i32x8 rowsum_ones8(int lane) {
+    const int m = lane & 15, kb = lane >> 4;
+    const int w = ((m & 3) == 0 && ((m >> 2) & 1) == (kb & 1)) ? 0x38383838 : 0;
+    return i32x8{w, w, w, w, w, w, w, w};
+}
+
 __device__ __forceinline__ float pair_max8(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -241,7 +283,7 @@ __device__ __forceinline__ float pair_sum8(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, int QTERMS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_fp8_kernel(Fp8Args a) {
     using TL = Tile8<D>;
@@ -278,6 +320,7 @@ void fwd_fp8_kernel(Fp8Args a) {
         const int b = bh / a.H, h = bh % a.H;
         const int64_t npad = fp8_npad(a.N);
         const uint8_t* Qg = a.q + int64_t(bh) * a.N * D;
+        const int64_t q_plane = int64_t(a.B) * a.H * a.N * D;   // offset of Q's residual term
         const uint8_t* Kg = a.k + int64_t(bh) * a.N * D;
         const uint8_t* Vg = a.vt + int64_t(bh) * D * npad;
         uint16_t* Og = static_cast<uint16_t*>(a.o) + int64_t(b) * a.osb + int64_t(h) * a.osh;
@@ -314,17 +357,24 @@ void fwd_fp8_kernel(Fp8Args a) {
             }
         };
 
-        // Q^T operand: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31]
-        i32x8 qreg[KS];
+        // Q^T operands: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31],
+        // of the first e4m3 term (qhi) and of the residual term (qlo, which
+        // the matrix core scales by 2^-4 through its E8M0 B-operand scale).
+        i32x8 qhi[KS], qlo[KS];
     #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+            uint4 h0 = make_uint4(0, 0, 0, 0), h1 = h0, l0 = h0, l1 = h0;
             if (qi < a.N) {
                 const uint8_t* p = Qg + int64_t(qi) * D + 64 * ks + 32 * hh;
-                lo = *reinterpret_cast<const uint4*>(p);
-                hi = *reinterpret_cast<const uint4*>(p + 16);
+                h0 = *reinterpret_cast<const uint4*>(p);
+                h1 = *reinterpret_cast<const uint4*>(p + 16);
+                if (QTERMS == 2) {
+                    l0 = *reinterpret_cast<const uint4*>(p + q_plane);
+                    l1 = *reinterpret_cast<const uint4*>(p + q_plane + 16);
+                }
             }
-            qreg[ks] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+            qhi[ks] = i32x8{int(h0.x), int(h0.y), int(h0.z), int(h0.w), int(h1.x), int(h1.y), int(h1.z), int(h1.w)};
+            qlo[ks] = i32x8{int(l0.x), int(l0.y), int(l0.z), int(l0.w), int(l1.x), int(l1.y), int(l1.z), int(l1.w)};
         }
         const float sq = (q0 < a.N) ? a.qs[int64_t(bh) * nqb + q0 / kQBlk] : 1.f;
         const float c2q = a.scale_log2 * sq;
@@ -335,34 +385,60 @@ void fwd_fp8_kernel(Fp8Args a) {
     #pragma unroll
             for (int g = 0; g < 16; ++g) oacc[dt][g] = 0.f;
         float m_ref = -FLT_MAX;  // log2 units of the true scaled score
-        float lsum = 0.f;        // this lane's share of sum(64 p)
+        float lsum = 0.f;        // the row's sum of the e4m3 values of 64 p
 
+        // K operand of score subtile st, k-step ks (two 16-byte LDS reads)
+        auto k_operand = [&](const char* kt_lds, int st, int ks) -> i32x8 {
+            const int row = krow8(j, st);
+            const char* rp = kt_lds + row * D;
+            const int sw = TL::kswz(row);
+            const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh) ^ sw));
+            const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh + 1) ^ sw));
+            return i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        };
+        // V^T operand of head-dim tile dt
+        auto v_operand = [&](const char* vt_lds, int dt) -> i32x8 {
+            const int row = 32 * dt + j;
+            const char* rp = vt_lds + row * BC;
+            const int sw = TL::vswz(row);
+            const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh) ^ sw));
+            const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh + 1) ^ sw));
+            return i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        };
+        // Score product q of a tile (0 .. 4 KS - 1): k-step q / 4, the residual
+        // term when bit 1 is set, subtile q & 1 -- consecutive products go to
+        // different accumulators, and each K operand serves two of them.
+        constexpr int NQK = (QTERMS == 2 ? 4 : 2) * KS;
+        auto score_mfma = [&](f32x16 (&s)[2], const i32x8 (&kop)[2], int q) {
+            const int st = q & 1, part = QTERMS == 2 ? (q >> 1) & 1 : 0, ks = QTERMS == 2 ? q >> 2 : q >> 1;
+            const f32x16 zero = {};
+            s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                kop[st], part ? qlo[ks] : qhi[ks], (q < 2) ? zero : s[st], 0, 0, 0, 127, 0, part ? 123 : 127);
+        };
         auto scores = [&](f32x16 (&s)[2], const char* kt_lds) {
+            i32x8 kop[2];
     #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-    #pragma unroll
-                for (int g = 0; g < 16; ++g) s[st][g] = 0.f;
-                const int row = krow8(j, st);
-                const char* rp = kt_lds + row * D;
-                const int sw = TL::kswz(row);
-    #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh) ^ sw));
-                    const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((4 * ks + 2 * hh + 1) ^ sw));
-                    const i32x8 ka = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-                    s[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qreg[ks], s[st], 0, 0, 0, 127, 0, 127);
+            for (int q = 0; q < NQK; ++q) {
+                if ((q & (QTERMS == 2 ? 3 : 1)) == 0) {
+                    kop[0] = k_operand(kt_lds, 0, q >> (QTERMS == 2 ? 2 : 1));
+                    kop[1] = k_operand(kt_lds, 1, q >> (QTERMS == 2 ? 2 : 1));
                 }
+                score_mfma(s, kop, q);
             }
         };
+        const i32x8 ones_a = rowsum_ones8(lane);
 
         i32x8 pb = {};   // e4m3 probabilities of a tile: the B operand of the PV product
+        // Block of tile kt: row maximum of S(kt) and the threshold rule, then
+        // the NQK score products of tile kt+1, each with a share of tile kt's
+        // probabilities beside it (fma, exp2, e4m3 pack) in fenced chunks; the
+        // row sum of the e4m3 values on the matrix core; the PV products.
         auto softmax_pv = [&](f32x16 (&s)[2], int kt, float ksc, float vsc, const char* vt_lds, f32x16 (&nxt)[2],
                               const char* knext) {
             const int k_lo = kt * BC;
             // lane half hh holds keys 32hh .. 32hh+31 of the tile: K block 2kt + hh
             const float ct = c2q * ksc;
-            const float sv = vsc;
-            const int e8v = (__float_as_uint(sv) >> 23) & 0xFF;  // power of two -> E8M0
+            const int e8v = (__float_as_uint(vsc) >> 23) & 0xFF;  // power of two -> E8M0
             if ((k_lo + BC > a.N) || (CAUSAL && k_lo + BC - 1 > q0)) {
                 const int lim = (CAUSAL ? min(qi, a.N - 1) : a.N - 1) - k_lo - 32 * hh;
     #pragma unroll
@@ -387,36 +463,44 @@ void fwd_fp8_kernel(Fp8Args a) {
                     for (int g = 0; g < 16; ++g) oacc[dt][g] *= alpha;
                 m_ref = mn;
             }
-            scores(nxt, knext);
             const float bias = 6.f - m_ref;  // exp2(s*ct - m + 6) = 64 p
-            float ls0 = 0.f, ls1 = 0.f;
+            // probabilities of chunk r4 (4 scores: subtile r4 / 4, elements 4 (r4 % 4) ..)
+            auto exp_chunk = [&](int r4) {
+                const int st = r4 >> 2, r = r4 & 3;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 0], ct, bias));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 1], ct, bias));
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 2], ct, bias));
+                const float p3 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 3], ct, bias));
+                // the low half is written here and the high half below, so the
+                // incoming word is irrelevant: it is the previous tile's
+                // (already consumed) word of the same register
+                const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[r4], false);
+                pb[r4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+            };
+            constexpr int CPM = 8 / NQK;   // probability chunks per score product
+            i32x8 kop[2];
+            __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
-            for (int st = 0; st < 2; ++st)
-    #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 0], ct, bias));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 1], ct, bias));
-                    const float p2 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 2], ct, bias));
-                    const float p3 = __builtin_amdgcn_exp2f(fmaf(s[st][4 * r + 3], ct, bias));
-                    ls0 += p0 + p1;
-                    ls1 += p2 + p3;
-                    // the low half is written here and the high half below, so
-                    // the incoming word is irrelevant: it is the previous tile's
-                    // (already consumed) word of the same register
-                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[4 * st + r], false);
-                    pb[4 * st + r] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+            for (int q = 0; q < NQK; ++q) {
+                if ((q & (QTERMS == 2 ? 3 : 1)) == 0) {
+                    kop[0] = k_operand(knext, 0, q >> (QTERMS == 2 ? 2 : 1));
+                    kop[1] = k_operand(knext, 1, q >> (QTERMS == 2 ? 2 : 1));
                 }
-            lsum += ls0 + ls1;
+                score_mfma(nxt, kop, q);
+    #pragma unroll
+                for (int c = 0; c < CPM; ++c) exp_chunk(q * CPM + c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const f32x4 rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                ones_a, pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            i32x8 va = v_operand(vt_lds, 0);
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int row = 32 * dt + j;
-                const char* rp = vt_lds + row * BC;
-                const int sw = TL::vswz(row);
-                const uint4 lo = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh) ^ sw));
-                const uint4 hi = *reinterpret_cast<const uint4*>(rp + 16 * ((2 * hh + 1) ^ sw));
-                const i32x8 va = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-                oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[dt], 0, 0, 0, e8v, 0, 127);
+                const i32x8 vcur = va;
+                if (dt + 1 < DT) va = v_operand(vt_lds, dt + 1);
+                oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vcur, pb, oacc[dt], 0, 0, 0, e8v, 0, 127);
             }
+            lsum += rs[0];
         };
 
         if (nt > 0) {
@@ -454,7 +538,7 @@ void fwd_fp8_kernel(Fp8Args a) {
         }
 
         if (qi < a.N && wnt > 0) {
-            const float lt = pair_sum8(lsum);
+            const float lt = lsum;   // the row sum already covers both lane halves
             const float inv = 1.0f / lt;
             uint16_t* orow = Og + int64_t(qi) * a.oss;
     #pragma unroll
@@ -485,7 +569,10 @@ int launch_a(const Fp8Args& a, hipStream_t s) {
     constexpr int NW = 8;
     const int n_qt = (a.N + NW * WQ - 1) / (NW * WQ);
     const int64_t grid = int64_t(CAUSAL ? (n_qt + 1) / 2 : n_qt) * a.B * a.H;
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, CAUSAL>), dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, s, a);
+    if (a.q_terms == 1)
+        hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, CAUSAL, 1>), dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, CAUSAL, 2>), dim3(static_cast<unsigned>(grid)), dim3(NW * 64), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -65,9 +65,31 @@ typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int BC = 64;  // keys per K/V tile
 constexpr int WQ = 32;  // query rows per wave
 constexpr bf16x2 kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+// Row sums of the probabilities on the matrix core (four small products per
+// tile) instead of the vector unit (sixteen v_dot2 per tile): measured +2.1 %
+// at head_dim 64 and +0.8 % at 128, where the vector work per score is the
+// limit ("FlashAttention-4" explainer, 論文 Section 3.2, moves work off the
+// exponential unit; here it moves off the vector unit).
+constexpr bool kRowsumMfma = true;
+
+// A operand of the row-sum product v_mfma_f32_16x16x32_bf16(A, P chunk, acc).
+// Fed as its B operand, the probability chunk of lane l (query l % 32, keys of
+// lane half l / 32) is column l % 16 of K-block l / 16; A row m holds ones in
+// the K-blocks whose parity is that of m / 4 when m % 4 == 0 and zeros
+// elsewhere, so output row 4g, column c -- register 0 of lane 16g + c -- is
+// the sum over both lane halves of query 16 (g % 2) + c = (16g + c) % 32:
+// every lane receives its own query's full 64-key row sum.
+__device__ __forceinline__ bf16x8 rowsum_ones(int lane) {
+    const int m = lane & 15, kb = lane >> 4;
+    const __bf16 v = static_cast<__bf16>(((m & 3) == 0 && ((m >> 2) & 1) == (kb & 1)) ? 1.0f : 0.0f);
+    return bf16x8{v, v, v, v, v, v, v, v};
+}
 
 template <int D>
 struct Tile {
@@ -187,7 +209,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
 #pragma unroll
         for (int g = 0; g < 16; ++g) oacc[dt][g] = 0.f;
     float m_ref = -FLT_MAX;  // log2 units
-    float lsum = 0.f;        // this lane's share of the running sum
+    float lsum = 0.f;        // running sum: this lane's share, or the row's with kRowsumMfma
+    const bf16x8 ones_a = rowsum_ones(lane);
     const float c2 = a.scale_log2;
 
     // per-lane LDS addressing that does not change across tiles
@@ -269,6 +292,13 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     // bf16 step of 2^tau, where either choice is exact).  An overflowing
     // exp2 gives an infinite sum and so also takes the slow path.
     const float thr = exp2f(a.tau);
+    // Does a partial row sum exceed 2^tau?  Compared as unsigned bit patterns,
+    // so that an infinite or NaN sum (an overflowing exp2 in the matrix-core
+    // row sum meets the zeros of its constant operand: 0 * inf = NaN) also
+    // takes the slow path; the sums are never negative.  A float comparison
+    // would not do: the kernels are compiled assuming no NaN operands.
+    const uint32_t thr_bits = __float_as_uint(thr);
+    auto over = [&](float lp) { return __any(__float_as_uint(lp) > thr_bits); };
     auto rescale = [&](const f32x16 (&s)[2]) -> bool {
         const float mt = tile_max(s) * c2;
         if (!__any(mt > m_ref + a.tau)) return false;
@@ -291,7 +321,11 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         const bf16x2 pr = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
         pb[c][e] = pr[0];
         pb[c][e + 1] = pr[1];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, acc, false);
+        if (!kRowsumMfma) acc = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, acc, false);
+    };
+    // the row sum of chunk c on the matrix core (kRowsumMfma)
+    auto chunk_sum = [&](const bf16x8 (&pb)[4], int c, f32x4& rs) {
+        rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_a, pb[c], rs, 0, 0, 0);
     };
 
     // One straight-line block per tile, issued in fenced chunks so that every
@@ -330,6 +364,7 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
 #pragma unroll
         for (int i = 0; i < NPK; ++i) kb[i] = k_operand(knext, i);
         float lpart[2] = {0.f, 0.f};  // two independent row-sum chains
+        f32x4 rs = {0.f, 0.f, 0.f, 0.f};
         const f32x16 zero = {};
         flush_deferred();
         __builtin_amdgcn_sched_barrier(0);
@@ -342,15 +377,20 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
             for (int q = 0; q < PPM; ++q) {
                 const int p = m * PPM + q;
                 exp_pair(s, p, pb, lpart[p & 1]);
+                if (kRowsumMfma && (p & 3) == 3) chunk_sum(pb, p >> 2, rs);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        float lp = lpart[0] + lpart[1];
-        if (__any(lp > thr) && rescale(s)) {
+        float lp = kRowsumMfma ? rs[0] : lpart[0] + lpart[1];
+        if (over(lp) && rescale(s)) {
             lpart[0] = lpart[1] = 0.f;
+            rs = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < NPAIR; ++p) exp_pair(s, p, pb, lpart[p & 1]);
-            lp = lpart[0] + lpart[1];
+            for (int p = 0; p < NPAIR; ++p) {
+                exp_pair(s, p, pb, lpart[p & 1]);
+                if (kRowsumMfma && (p & 3) == 3) chunk_sum(pb, p >> 2, rs);
+            }
+            lp = kRowsumMfma ? rs[0] : lpart[0] + lpart[1];
         }
         lsum += lp;
         bf16x8 vb[NPV];
@@ -406,7 +446,7 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
     if (qi < a.N && wnt > 0) {
-        const float lt = pair_sum(lsum);
+        const float lt = kRowsumMfma ? lsum : pair_sum(lsum);
         const float inv = 1.0f / lt;
         u16* orow = Og + int64_t(qi) * a.ss;
 #pragma unroll

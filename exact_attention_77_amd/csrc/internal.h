@@ -49,6 +49,7 @@ struct Fp8Args {
     float tau;
     int32_t causal;
     int32_t tile_cfg;
+    int32_t q_terms;       // 1: Q's first e4m3 term only; 2: both terms
 };
 
 // Backward arguments (bf16 tensors sharing one layout; fp32 workspace of two

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FLASH_ATTN_ABI_VERSION 1
+#define FLASH_ATTN_ABI_VERSION 2
 
 typedef enum flash_attn_status {
     FLASH_ATTN_OK = 0,
@@ -87,11 +87,16 @@ typedef struct flash_attn_layout {
  * tile_cfg: 0 = automatic (bf16: 4-wave workgroups of 128 query rows for
  *   head_dim 64, 8-wave workgroups of 256 rows for 128); 1 and 2 force the
  *   8- and 4-wave forms of the bf16 kernel; any other value is an argument
- *   error.  The result does not depend on it beyond fp32 summation order. */
+ *   error.  The result does not depend on it beyond fp32 summation order.
+ * fp8_q_terms: flash_attn_fwd_fp8 only (ignored elsewhere): 0 or 2 = use both
+ *   e4m3 terms of Q (the default: Q K^T then carries only K's rounding), 1 =
+ *   Q's first term only (four fewer fp8 products per 64-key tile at d = 128,
+ *   about 11 % faster, the error of a single e4m3 rounding of Q); other
+ *   values are an argument error. */
 typedef struct flash_attn_fwd_opts {
     float tau_log2;
     int32_t tile_cfg;
-    int32_t reserved;   /* must be 0 */
+    int32_t fp8_q_terms;
 } flash_attn_fwd_opts;
 
 /*
@@ -121,7 +126,12 @@ flash_attn_status flash_attn_fwd(const void* q, const void* k, const void* v,
  * saturating at +-448).  The role fixes the block size, the scale rule and the
  * output layout the fp8 attention kernel consumes:
  *   Q: blocks of 32 rows, scale = amax(block)/448 (1 for an all-zero block),
- *      output contiguous [B, H, N, d];
+ *      output two contiguous planes [2][B, H, N, d]: plane 0 holds
+ *      hi = e4m3(x / scale), plane 1 the residual term
+ *      lo = e4m3(16 (x / scale - hi)), so that x = scale (hi + lo / 16) to
+ *      about 2^-8 relative (the attention kernel applies the 1/16 as a matrix
+ *      core operand scale; Q K^T then carries the error of K's single term
+ *      only);
  *   K: blocks of 32 rows, same scale rule, output contiguous [B, H, N, d];
  *   V: blocks of 64 rows, scale = the smallest power of two >= amax/448 (so the
  *      matrix cores apply it as an exponent), never rotated, output TRANSPOSED
@@ -153,14 +163,22 @@ size_t flash_attn_fp8_buffer_bytes(flash_attn_layout layout, flash_attn_fp8_role
 int64_t flash_attn_fp8_num_scales(flash_attn_layout layout, flash_attn_fp8_role role);
 
 /*
- * FP8 forward attention on the pre-pass outputs: e4m3 Q, K (contiguous
+ * FP8 forward attention ("FlashAttention-3: Fast and Accurate Attention with
+ * Asynchrony and Low-precision", sec. 技術 3: e4m3 operands with per-block
+ * scales, which a blockwise kernel applies at no extra cost; the exp cost
+ * relative to the doubled matrix rate is the point of its 考察) on the
+ * pre-pass outputs: e4m3 Q (the two planes [2][B, H, N, d]), K (contiguous
  * [B, H, N, d]) and V (transposed [B, H, d, N_pad]) with their block scales;
  * the matrix products run on the fp8 matrix cores with fp32 accumulation.  Q/K
- * block scales fold into the softmax exponent, the power-of-two V scales are
- * applied by the matrix cores, and the probabilities enter the second product
- * as e4m3(64 p) (p <= 2^2.5: tau is capped at 2.5 here); the row sum uses the
- * fp32 p.  O is bf16 with the strides of `o_layout`, whose batch, heads,
- * seqlen and head_dim give the shape of everything; LSE is fp32 [B, H, N].
+ * block scales fold into the softmax exponent, the power-of-two V scales and
+ * the 1/16 of Q's residual term are applied by the matrix cores, and the
+ * probabilities enter the second product as e4m3(64 p) (p <= 2^2.5: tau is
+ * capped at 2.5 here).  The row sum adds the same e4m3 values that multiply V
+ * (so O is normalised by the sum of its own weights), on the matrix core.
+ * O is bf16 with the strides of `o_layout`, whose batch, heads, seqlen and
+ * head_dim give the shape of everything; LSE is fp32 [B, H, N], the natural
+ * log of that row sum (within ln(1 + 2^-4) of the exact one of the
+ * quantised scores).
  */
 flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                                      const float* q_scale, const float* k_scale,

@@ -30,11 +30,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.flash_attn_abi_version() == 1
+    assert fa.flash_attn_abi_version() == 2
     for code, name in fa.STATUS.items():
         assert fa.flash_attn_status_str(code) == name
     lay = _lay(B=2, H=3, N=130, d=128)
-    assert fa.flash_attn_fp8_buffer_bytes(lay, fa.ROLE_Q) == 2 * 3 * 130 * 128
+    assert fa.flash_attn_fp8_buffer_bytes(lay, fa.ROLE_Q) == 2 * 2 * 3 * 130 * 128   # code + residual term
+    assert fa.flash_attn_fp8_buffer_bytes(lay, fa.ROLE_K) == 2 * 3 * 130 * 128
     assert fa.flash_attn_fp8_buffer_bytes(lay, fa.ROLE_V) == 2 * 3 * 192 * 128   # padded to 64 keys
     assert fa.flash_attn_fp8_num_scales(lay, fa.ROLE_Q) == 2 * 3 * 5
     assert fa.flash_attn_fp8_num_scales(lay, fa.ROLE_K) == 2 * 3 * 5
@@ -132,7 +133,7 @@ def test_bad_causal_flag():
 
 @pytest.mark.parametrize("opts", [fa.FwdOpts(65.0, 0, 0), fa.FwdOpts(float("nan"), 0, 0),
                                   fa.FwdOpts(8.0, 9, 0), fa.FwdOpts(8.0, 3, 0), fa.FwdOpts(8.0, -1, 0),
-                                  fa.FwdOpts(8.0, 0, 1)])
+                                  fa.FwdOpts(8.0, 0, 3), fa.FwdOpts(8.0, 0, -1)])
 def test_bad_options(opts):
     assert fwd(opts=ctypes.byref(opts)) == 6
 

@@ -35,7 +35,7 @@ def test_fwd_rejects_bad_lse_and_out():
 
 def _fp8_inputs(B=1, H=2, N=100, d=128):
     npad = (N + 63) // 64 * 64
-    q8 = torch.zeros((B, H, N, d), dtype=torch.uint8)
+    q8 = torch.zeros((2, B, H, N, d), dtype=torch.uint8)
     k8 = torch.zeros((B, H, N, d), dtype=torch.uint8)
     v8 = torch.zeros((B, H, d, npad), dtype=torch.uint8)
     qs = torch.ones((B, H, (N + 31) // 32))
@@ -46,6 +46,12 @@ def _fp8_inputs(B=1, H=2, N=100, d=128):
 
 def test_fwd_fp8_rejects_host_tensors():
     assert _status(fa.flash_attn_fwd_fp8, *_fp8_inputs()) == ERR_ARG
+
+
+def test_fwd_fp8_rejects_single_plane_q():
+    a = _fp8_inputs()
+    a[0] = a[0][0].contiguous()                          # [B, H, N, d]: the residual plane missing
+    assert _status(fa.flash_attn_fwd_fp8, *a) == ERR_SHAPE
 
 
 def test_fwd_fp8_rejects_unpadded_v():

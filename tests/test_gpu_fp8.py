@@ -62,6 +62,29 @@ def _check_codes(gpu_codes, x_rot, scales, block, x_src):
         assert np.all(np.abs(yy - mid) <= bound), "non-tie code mismatch"
 
 
+def _check_residual_term(hi, lo, x_rot, scales, block, x_src):
+    """Q's second term: lo = e4m3(16 (y - hi)) with y = x_rot / scale, so that
+    |hi + lo/16 - y| <= (half an e4m3 step of 16 |y - hi|) / 16, i.e. at most
+    2^-4 |y - hi| + 2^-14 (subnormal steps of 2^-9), plus the fp32 error of y
+    (the rotation's sums, bounded as in _check_codes)."""
+    d = x_rot.shape[-1]
+    rep = np.repeat(scales, block, axis=2)[:, :, :x_rot.shape[2], None]
+    y = np.clip(x_rot / rep, -448, 448)
+    vh = oracle.e4m3_decode(hi)
+    vl = oracle.e4m3_decode(lo)
+    assert np.all(np.abs(16 * (y - vh)) <= 256 + 1e-3)
+    l1 = np.broadcast_to(np.abs(x_src).sum(axis=-1, keepdims=True), x_src.shape)
+    fp32 = 4e-6 * l1 / np.sqrt(d) / np.broadcast_to(rep, y.shape) + 1e-7 * np.abs(y)
+    err = np.abs(vh + vl / 16 - y)
+    bound = 2.0 ** -4 * np.abs(y - vh) + 2.0 ** -14 + 1.07 * fp32
+    assert np.all(err <= bound), float(np.max(err / bound))
+    # the two terms together are about 16 times closer than the first alone
+    e1 = np.sqrt(np.mean((vh - y) ** 2))
+    e2 = np.sqrt(np.mean(err ** 2))
+    print(f"Q residual term: rms error {e1:.3e} -> {e2:.3e}", flush=True)
+    assert e2 <= e1 / 8
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 100, 300])
@@ -79,7 +102,13 @@ def test_quantize_q_k_rotated(dtype, d, N):
         _, osc = oracle.quantize_blocks(xr, block)
         g = sc.cpu().numpy().astype(np.float64)
         assert np.max(np.abs(g - osc) / osc) <= 2e-6
-        _check_codes(codes.cpu().numpy(), xr, osc, block, xref)
+        c = codes.cpu().numpy()
+        if role == fa.ROLE_Q:
+            assert c.shape == (2,) + xr.shape
+            _check_codes(c[0], xr, osc, block, xref)
+            _check_residual_term(c[0], c[1], xr, osc, block, xref)
+        else:
+            _check_codes(c, xr, osc, block, xref)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -100,7 +129,7 @@ def test_quantize_v_transposed_pow2(d, N):
     _check_codes(np.ascontiguousarray(c[:, :, :, :N].transpose(0, 1, 3, 2)), vref, osc, 64, vref)
 
 
-def _fp8_run(q, k, v, causal, d, signs, in_dtype="f32"):
+def _fp8_run(q, k, v, causal, d, signs, in_dtype="f32", q_terms=2):
     import exact_attention_77_amd as fa
     torch = _t()
     sdev = torch.from_numpy(signs).cuda()
@@ -110,10 +139,12 @@ def _fp8_run(q, k, v, causal, d, signs, in_dtype="f32"):
     q8, qs = fa.flash_attn_fp8_quantize(qd, fa.ROLE_Q, rotate=True, signs=sdev)
     k8, ks = fa.flash_attn_fp8_quantize(kd, fa.ROLE_K, rotate=True, signs=sdev)
     v8, vs = fa.flash_attn_fp8_quantize(vd, fa.ROLE_V)
-    o, lse = fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal)
+    o, lse = fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, q_terms=q_terms)
     torch.cuda.synchronize()
     N = q.shape[2]
-    deq_q = oracle.e4m3_decode(q8.cpu().numpy()) * np.repeat(qs.cpu().numpy().astype(np.float64), 32, 2)[:, :, :N, None]
+    q8c = q8.cpu().numpy()   # the code and its residual term (1/16)
+    qv = oracle.e4m3_decode(q8c[0]) + (oracle.e4m3_decode(q8c[1]) / 16.0 if q_terms == 2 else 0.0)
+    deq_q = qv * np.repeat(qs.cpu().numpy().astype(np.float64), 32, 2)[:, :, :N, None]
     deq_k = oracle.e4m3_decode(k8.cpu().numpy()) * np.repeat(ks.cpu().numpy().astype(np.float64), 32, 2)[:, :, :N, None]
     vt = oracle.e4m3_decode(v8.cpu().numpy()[:, :, :, :N]).transpose(0, 1, 3, 2)
     deq_v = vt * np.repeat(vs.cpu().numpy().astype(np.float64), 64, 2)[:, :, :N, None]
@@ -180,13 +211,14 @@ def _check_kernel_only(o, lse, deq, causal, report=print):
     assert r_o.max() <= 1.0 and r_l.max() <= 1.0
 
 
+@pytest.mark.parametrize("q_terms", [2, 1])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [64, 300, 777])
-def test_fp8_attention_accuracy(causal, d, N):
+def test_fp8_attention_accuracy(causal, d, N, q_terms):
     q, k, v = normal_qkv(1, 2, N, d, 700 + N + d, outliers=True)
     signs = hadamard_signs(d)
-    o, lse, deq = _fp8_run(q, k, v, causal, d, signs)
+    o, lse, deq = _fp8_run(q, k, v, causal, d, signs, q_terms=q_terms)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     o_ex, _ = oracle.attn_fwd(q, k, v, causal=causal)
     o_r1, _ = oracle.fp8_per_tensor_baseline(q, k, v, causal=causal)
@@ -198,25 +230,26 @@ def test_fp8_attention_accuracy(causal, d, N):
     _check_kernel_only(o, lse, deq, causal)
 
 
-def _fp8_full_size():
+def _fp8_full_size(q_terms=2):
     w = WORKLOADS["fp8_n8192_d128"]
-    print(f"fp8 full size B{w.B} H{w.H} N{w.N} d{w.d}", flush=True)
+    print(f"fp8 full size B{w.B} H{w.H} N{w.N} d{w.d} q_terms={q_terms}", flush=True)
     q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=True)
-    o, lse, deq = _fp8_run(q, k, v, False, w.d, hadamard_signs(w.d))
+    o, lse, deq = _fp8_run(q, k, v, False, w.d, hadamard_signs(w.d), q_terms=q_terms)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     return (q, k, v), o, lse, deq
 
 
-def test_fp8_full_size_accuracy_all_rows(margin):
+@pytest.mark.parametrize("q_terms", [2, 1])
+def test_fp8_full_size_accuracy_all_rows(margin, q_terms):
     """B=2 H=16 N=8192 d=128 non-causal with outliers, every row: RMSE against
     exact attention on the unquantised inputs <= 5e-2 and below the
-    per-tensor fp8 baseline's."""
-    (q, k, v), o, _, _ = _fp8_full_size()
+    per-tensor fp8 baseline's (both forms of Q)."""
+    (q, k, v), o, _, _ = _fp8_full_size(q_terms)
     o_ex, _ = oracle.attn_fwd(q, k, v)
     rmse = float(np.sqrt(np.mean((o - o_ex) ** 2)))
     o_r1, _ = oracle.fp8_per_tensor_baseline(q, k, v)
     rmse_r1 = float(np.sqrt(np.mean((o_r1 - o_ex) ** 2)))
-    margin(f"fp8_n8192_d128 all rows: RMSE fp8 kernel {rmse:.4e} (bar 5e-2, {rmse / 5e-2:.0%})  "
+    margin(f"fp8_n8192_d128 q_terms={q_terms} all rows: RMSE fp8 kernel {rmse:.4e} (bar 5e-2, {rmse / 5e-2:.0%})  "
            f"per-tensor baseline {rmse_r1:.4e}")
     assert rmse <= 5e-2 and rmse < rmse_r1
 
