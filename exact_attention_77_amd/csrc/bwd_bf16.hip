@@ -15,20 +15,17 @@
 // Two kernels, both on the caller's stream, the dQ kernel first:
 //  1. dQ   : (below) also forms, per query row, -D_i and LSE_i * log2(e) (fp32)
 //            and stores them in the workspace for the dK/dV kernel.
-//  2. dK/dV: one workgroup per (batch, head, 128-key tile), eight waves; wave
-//            w works on key block w % 4 (32 keys) and query half w / 4 of each
-//            64-query tile of Q and dO, staged in LDS by direct global->LDS
-//            loads (double-buffered).  Per tile, with v_mfma_f32_32x32x16_bf16:
+//  2. dK/dV: one workgroup per (batch, head, 128-key tile), four waves of 32
+//            keys each (one wave per SIMD); a wave keeps its keys' K and V rows
+//            in registers and streams 64-query tiles of Q and dO (with their
+//            statistics) through LDS by direct global->LDS loads
+//            (double-buffered).  Per tile, with v_mfma_f32_32x32x16_bf16:
 //              S = Q K^T and dP - D (the accumulator starts at -D); in the
 //              32x32 accumulator layout a lane holds ONE key and 16 queries;
-//              P = exp2(S * scale*log2e - LSE*log2e), dS = P (dP - D) -> bf16,
-//              both stored transposed (row = key) to LDS;
-//              then the wave of query half 0 accumulates dV^T += dO^T P and
-//              the one of half 1 dK^T += Q^T dS over the whole 64-query tile
-//              (dO^T, Q^T by transposing LDS reads; P^T, dS^T by row reads).
-//              Half of those products is issued in the next tile's step,
-//              beside its exp/dS work, so that this vector work has matrix
-//              work next to it.
+//              P = exp2(S * scale*log2e - LSE*log2e), dS = P (dP - D) -> bf16
+//              are, thanks to the query order of the A operand, directly the
+//              B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by
+//              transposing LDS reads) -- no exchange through LDS.
 //  dQ kernel: one workgroup per (batch, head, 256-query tile), eight waves of
 //            32 queries, K/V tiles of 64 keys streamed through LDS (the loop
 //            order of the forward pass); each query row belongs to exactly one
@@ -69,12 +66,9 @@ typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
-constexpr int BK = 128;  // keys per workgroup (32 per wave)
-constexpr int BQ = 64;   // queries per tile of the inner loop (32 per wave)
+constexpr int BK = 128;  // keys per dK/dV workgroup (32 per wave)
+constexpr int BQ = 64;   // queries per tile of the dK/dV inner loop (two 32-query subtiles)
 constexpr float kLog2e = 1.4426950408889634f;
-// s_waitcnt immediate for lgkmcnt(0) alone (gfx9 encoding: vmcnt bits 3:0
-// and 15:14, expcnt 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
-constexpr int kWaitLds = 0xC07F;
 
 // XOR swizzle (16-byte chunk units) of a row of a Q, dO or K tile in LDS.  A
 // tile is read two ways: by rows (16 lanes read one chunk of 16 rows) and
@@ -104,35 +98,34 @@ __device__ __forceinline__ bf16x8 cat(short4_t lo, short4_t hi) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV kernel: 8 waves; wave w works on key block kb = w % 4 (32 keys) and
-// query half qh = w / 4 (32 of the tile's 64 queries) for S, dP, P and dS; the
-// wave with qh = 0 accumulates dV of its key block, the one with qh = 1 dK.
+// dK/dV kernel: 4 waves of 32 keys (one wave per
+// SIMD).  A wave keeps its keys' K and V rows in registers and, per 64-query
+// tile of Q / dO (staged in LDS as above), computes S = Q K^T and dP - D for
+// all 64 queries in two 32-query subtiles.  With the Q / dO rows fed in the
+// bit-2/3-swapped order, the accumulator registers of subtile qs hold, for
+// the lane's key, queries 32qs + 16c' + 8hh .. +7 in registers 8c' .. 8c'+7:
+// after exp2 and the bf16 conversion they are directly the B operands of
+// dV^T += dO^T P and dK^T += Q^T dS for the 16-query chunks 2qs + c' (A
+// operands dO^T, Q^T by transposing LDS reads).  Nothing goes back through
+// LDS, and each Q / dO row is read by the 4 waves of the workgroup instead of
+// 8.  The two 128-register accumulators leave room for the operands only at
+// one wave per SIMD.  The subtiles are pipelined so that the exp/dS work of
+// one sits beside the products of the other.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int KS = D / 16;          // k-steps over the head dim
     constexpr int DT = D / 32;          // 32-column head-dim tiles
     constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int NWV = 4;              // waves: 32 keys each
     constexpr int QT_BYTES = BQ * D * 2;
-    constexpr int KT_BYTES = BK * D * 2;
-    constexpr int NQB = BQ * CPR / 64 / 8;   // 1 KB copy blocks per wave, Q (and dO) tile
-    constexpr int NKB = BK * CPR / 64 / 8;   // 1 KB copy blocks per wave, K tile
-    constexpr int PT_BYTES = BK * BQ * 2;    // P^T or dS^T: [128 keys][64 queries] bf16
-    static_assert(NQB >= 1 && NKB >= 1, "tile shape");
+    constexpr int NQB = QT_BYTES / 1024 / NWV;   // 1 KB copy blocks per wave, Q (and dO) tile
+    static_assert(NQB >= 1 && BK == 32 * NWV, "tile shape");
 
-    // Every LDS buffer is its own object: the compiler then knows that the
-    // direct-to-LDS prefetch into one buffer never aliases reads or writes of
-    // another and does not make them wait for it.
     __shared__ __attribute__((aligned(1024))) char qtile0[QT_BYTES], qtile1[QT_BYTES];   // Q, 64 rows
     __shared__ __attribute__((aligned(1024))) char otile0[QT_BYTES], otile1[QT_BYTES];   // dO, 64 rows
-    __shared__ __attribute__((aligned(1024))) char ktile[KT_BYTES];                      // K, 128 rows
-    // Per-row statistics of the tile (64 LSE*log2e, then 64 -D), per buffer.
-    __shared__ __attribute__((aligned(16))) float stat0[2 * BQ], stat1[2 * BQ];
-    // P^T then dS^T ([128 keys][64 queries] bf16 each).
-    __shared__ __attribute__((aligned(1024))) char ptbuf[2 * PT_BYTES];
+    __shared__ __attribute__((aligned(16))) float stat0[2 * BQ], stat1[2 * BQ];          // LSE*log2e, -D
 
-    // Key tile kt meets the queries from kt*BK on (causal): a workgroup takes
-    // the pair (p, n_kt-1-p) of one head so that all carry the same work.
     const int BH = a.B * a.H;
     const int n_kt = (a.N + BK - 1) / BK;
     const int kp = blockIdx.x / BH;
@@ -153,32 +146,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int kb = wave & 3, qh = wave >> 2;
         const int j = lane & 31, hh = lane >> 5;
         const int k0 = kt * BK;
-        const int kw0 = k0 + 32 * kb;                 // first key of this wave
+        const int kw0 = k0 + 32 * wave;               // first key of this wave
         const int key = kw0 + j;                      // this lane's key
-        const int key_c = min(key, a.N - 1);          // rows past the end re-read the last row
+        const int key_c = min(key, a.N - 1);          // keys past the end re-read the last row
 
-        // ---- K tile -> LDS; V rows -> registers ----------------------------------
-    #pragma unroll
-        for (int i = 0; i < NKB; ++i) {
-            const int blk = wave * NKB + i;
-            const int c = blk * 64 + lane;
-            const int row = c / CPR, pch = c % CPR;
-            const int64_t off = int64_t(min(k0 + row, a.N - 1)) * a.ss + 8 * (pch ^ swz<D>(row));
-            copy16_to_lds(Kg + off, ktile + blk * 1024);
-        }
-        // B operand of dO V^T: lane (key, half hh), k-step ks holds columns
-        // 16ks + 8hh .. +7 of the key's V row (K comes from the LDS tile).
-        bf16x8 vreg[KS];
+        // B operands of S = Q K^T and dP = dO V^T: lane (key, half hh), k-step
+        // ks holds columns 16ks + 8hh .. +7 of the key's K and V rows
+        bf16x8 kreg[KS], vreg[KS];
     #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int64_t off = int64_t(key_c) * a.ss + 16 * ks + 8 * hh;
+            kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + off));
             vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + off));
         }
 
-        // ---- Q / dO / statistics tile copy (direct to LDS, swizzled rows) -------
         auto copy_q = [&](int q0, auto bufc) {
             constexpr int buf = decltype(bufc)::value;
     #pragma unroll
@@ -198,239 +181,177 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 copy4_to_lds(a.ws_nd + int64_t(bh) * a.N + qq, st + BQ);
         };
 
-        // ---- per-lane LDS offsets ----------------------------------------------
-        // Everything that varies with the buffer, the k-step or the 16-row block
-        // is a compile-time immediate; what remains is a handful of per-lane
-        // offsets (the XOR swizzles of rows 16c + r do not depend on c).
-        const int prow = 32 * qh + perm_row(j);                        // Q / dO row-operand row
-        const int krow = 32 * kb + j;                                  // K / P^T / dS^T row of this lane's key
+        // ---- per-lane LDS offsets (the swizzle of row 32qs + prow does not depend on qs)
+        const int prow = perm_row(j);
         const int tr_row = 8 * hh + ((lane >> 2) & 3);                 // + 16 c  (+4 for the second read)
         const int tr_lch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dt
         const int tr_half = 8 * (lane & 1);
-        // P^T / dS^T: 128-byte rows (64 queries) of 8-byte pieces; the 16-byte
-        // chunk is XOR-swizzled by row (key).  Lanes 0..31 of a wave write or
-        // read one chunk of rows 0..31: eight consecutive keys get eight
-        // different chunks (the 16-byte writes go eight lanes at a time), and
-        // in sixteen consecutive keys no two of the same parity share a chunk
-        // (what the 16-byte row reads need).  Measured: no LDS bank conflicts.
-        auto pt_swz = [](int row) { return 2 * ((row & 7) ^ ((row >> 3) & 1)); };
-        int qo[KS], ko[KS];           // row operands: Q/dO rows prow, K rows krow
+        int qo[KS];
     #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qo[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
-            ko[ks] = krow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(krow));
-        }
-        int tro[DT][2];               // transposed reads, rows tr_row (+4) of column block dt
+        for (int ks = 0; ks < KS; ++ks) qo[ks] = prow * (2 * D) + 16 * ((2 * ks + hh) ^ swz<D>(prow));
+        int tro[DT][2];
     #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
     #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int r = tr_row + 4 * e;
-                tro[dt][e] = r * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(r));
+                const int rr = tr_row + 4 * e;
+                tro[dt][e] = rr * (2 * D) + tr_half + 16 * ((4 * dt + tr_lch) ^ swz<D>(rr));
             }
-        int pto[BQ / 16];             // P^T row reads (dS^T: + PT_BYTES)
-    #pragma unroll
-        for (int c = 0; c < BQ / 16; ++c) pto[c] = krow * 128 + 8 * ((4 * c + 2 * hh) ^ pt_swz(krow));
-        // P^T row writes (dS^T: + PT_BYTES): 16 bytes = queries 32qh + 16c + 8hh .. +7
-        // (the swizzle is even, so pieces p and p + 1 stay adjacent and in order)
-        int pwo[2];
-    #pragma unroll
-        for (int c = 0; c < 2; ++c) pwo[c] = krow * 128 + 8 * ((8 * qh + 4 * c + 2 * hh) ^ pt_swz(krow));
         auto ld16 = [](const char* t, int off) { return *reinterpret_cast<const bf16x8*>(t + off); };
         auto ldtr = [](const char* t, int lo, int hi) { return cat(lds_read_tr(t + lo), lds_read_tr(t + hi)); };
 
-        f32x16 acc[DT];   // dV^T (qh = 0) or dK^T (qh = 1) of this wave's 32 keys
+        // dV^T and dK^T of this wave's 32 keys.  Started by a product of zeros,
+        // so that they live in the accumulation registers from the start (zero
+        // vector registers here would make the allocator copy all 128 values
+        // into them before every tile's products).
+        f32x16 accv[DT], acck[DT];
+        {
+            const bf16x8 z = {};
+            const f32x16 z16 = {};
     #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) acc[dt][g] = 0.f;
+            for (int dt = 0; dt < DT; ++dt) {
+                accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, z16, 0, 0, 0);
+                acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, z16, 0, 0, 0);
+            }
+        }
 
         const float c2 = a.scale_log2;
         const int n_qt = (a.N + BQ - 1) / BQ;
         const int qt0 = CAUSAL ? k0 / BQ : 0;
 
-        // dV^T += dO^T P (qh = 0) or dK^T += Q^T dS (qh = 1) over the tile's 64
-        // queries: 16-query chunk c, head-dim tile dt.  The A operand is read
-        // transposed from the tile's Q or dO buffer, the B operand (P^T or
-        // dS^T rows of this wave's keys) from the exchange buffer.
-        constexpr int NP = BQ / 16 * DT;   // products per tile
-        constexpr int NEARLY = NP / 2;     // issued in the tile's own step
-        constexpr int NLATE = NP - NEARLY; // issued in the next step, beside its vector work
-        auto a_operand = [&](const char* at, int n) {
-            const int c = n / DT, dt = n % DT;
-            return ldtr(at, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
-        };
-        const int BO = qh ? PT_BYTES : 0;
-        bf16x8 late_b[NLATE / DT];   // B operands of the deferred chunks (read before the barrier)
-        // the deferred products of the previous tile, A operands from its buffer
-        // (not overwritten before this step's prefetch), n = NEARLY .. NP-1
-        auto late_mfma = [&](const char* at_prev, int i, bf16x8 (&op)[3]) {
-            const int n = NEARLY + i;
-            if (i + 2 < NLATE) op[(i + 2) % 3] = a_operand(at_prev, n + 2);
-            acc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], late_b[n / DT - NEARLY / DT], acc[n % DT], 0, 0, 0);
-        };
-
-        if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
-        // One query tile; `bufc` carries the LDS buffer as a compile-time constant
-        // (the loop below is unrolled by two) so that the compiler can tell the
-        // prefetch target from the buffer being read and does not wait for it.
-        // With `latec` true the previous tile (in the other buffer) left NLATE
-        // products to this step.
-        auto step = [&](int it, auto bufc, auto latec) {
+        // One 64-query tile `it` from buffer `buf`.
+        auto tile = [&](int it, auto bufc) {
             constexpr int buf = decltype(bufc)::value;
-            constexpr bool LATE = decltype(latec)::value;
-            const int qt_base = it * BQ;
-            const int q0 = qt_base + 32 * qh;         // first query of this wave
-            // tile `it` is in LDS; every wave is done with the previous P^T / dS^T
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_s_barrier();
             const char* qt = buf ? qtile1 : qtile0;
             const char* ot = buf ? otile1 : otile0;
-            const char* at_prev = qh ? (buf ? qtile0 : qtile1) : (buf ? otile0 : otile1);
-            const float* ls = (buf ? stat1 : stat0) + 32 * qh;
-
-            // S = Q K^T and dP - D (register g = 4r + t of lane half hh: query
-            // q0 + 16(r>>1) + 8hh + 4(r&1) + t, key `key`)
-            f32x16 s, dp;
+            const float* ls = buf ? stat1 : stat0;
+            const int q0 = it * BQ;
+            // S and dP - D of subtile qs: 2*KS products alternating, LDS
+            // operands read two ahead; `beside(m)` is issued after product m
+            auto sdp = [&](int qs, f32x16& sc, f32x16& dp, auto&& beside) {
     #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float4 nd = *reinterpret_cast<const float4*>(ls + BQ + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
-                dp[4 * r + 0] = nd.x; dp[4 * r + 1] = nd.y; dp[4 * r + 2] = nd.z; dp[4 * r + 3] = nd.w;
-            }
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float4 nd = *reinterpret_cast<const float4*>(ls + BQ + 32 * qs + 16 * (rr >> 1) + 8 * hh + 4 * (rr & 1));
+                    dp[4 * rr + 0] = nd.x; dp[4 * rr + 1] = nd.y; dp[4 * rr + 2] = nd.z; dp[4 * rr + 3] = nd.w;
+                }
     #pragma unroll
-            for (int g = 0; g < 16; ++g) s[g] = 0.f;
-            {   // 2*KS products alternating S / dP - D; LDS operands read two ahead
-                auto srcA = [&](int m) { return ld16((m & 1) ? ot : qt, qo[m >> 1]); };
-                bf16x8 opA[3], opK[3];
-                opA[0] = srcA(0); opK[0] = ld16(ktile, ko[0]);
-                opA[1] = srcA(1);
+                for (int g = 0; g < 16; ++g) sc[g] = 0.f;
+                auto src = [&](int m) { return ld16((m & 1) ? ot : qt, 32 * qs * 2 * D + qo[m >> 1]); };
+                bf16x8 op[3];
+                op[0] = src(0);
+                op[1] = src(1);
                 __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
                 for (int m = 0; m < 2 * KS; ++m) {
-                    if (m + 2 < 2 * KS) {
-                        opA[(m + 2) % 3] = srcA(m + 2);
-                        if (!(m & 1)) opK[(m + 2) % 3] = ld16(ktile, ko[(m + 2) >> 1]);
-                    }
+                    if (m + 2 < 2 * KS) op[(m + 2) % 3] = src(m + 2);
                     if (m & 1)
-                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], vreg[m >> 1], dp, 0, 0, 0);
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], vreg[m >> 1], dp, 0, 0, 0);
                     else
-                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[m % 3], opK[m % 3], s, 0, 0, 0);
+                        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], kreg[m >> 1], sc, 0, 0, 0);
+                    beside(m);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-
-            // masked (query, key) pairs get score -inf, hence P = 0
-            const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 32 > a.N || kw0 + 32 > a.N;
-            if (edge) {  // wave-uniform: diagonal or ragged blocks only
-                const int lo = CAUSAL ? key - q0 - 8 * hh : -(1 << 30);
-                const int hi = key < a.N ? a.N - 1 - q0 - 8 * hh : -1;
+            };
+            // masked (query, key) pairs of subtile qs get score -inf, hence P = 0
+            auto mask = [&](int qs, f32x16& sc) {
+                const int q0s = q0 + 32 * qs;
+                const bool edge = (CAUSAL && q0s < kw0 + 31) || q0s + 32 > a.N || kw0 + 32 > a.N;
+                if (edge) {   // wave-uniform: diagonal or ragged blocks only
+                    const int lo = CAUSAL ? key - q0s - 8 * hh : -(1 << 30);
+                    const int hi = key < a.N ? a.N - 1 - q0s - 8 * hh : -1;
     #pragma unroll
-                for (int g = 0; g < 16; ++g) {
-                    const int r = g >> 2, t = g & 3;
-                    const int off = 16 * (r >> 1) + 4 * (r & 1) + t;
-                    if (off < lo || off > hi) s[g] = -INFINITY;
+                    for (int g = 0; g < 16; ++g) {
+                        const int rr = g >> 2, t = g & 3;
+                        const int off = 16 * (rr >> 1) + 4 * (rr & 1) + t;
+                        if (off < lo || off > hi) sc[g] = -INFINITY;
+                    }
                 }
-            }
-            float l2[16];
+            };
+            // P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 for
+            // registers g0 .. g1-1 of subtile qs
+            bf16x8 pb[2][2], dsb[2][2];
+            float l2v[2][16];
     #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float4 v4 = *reinterpret_cast<const float4*>(ls + 16 * (r >> 1) + 8 * hh + 4 * (r & 1));
-                l2[4 * r + 0] = v4.x; l2[4 * r + 1] = v4.y; l2[4 * r + 2] = v4.z; l2[4 * r + 3] = v4.w;
-            }
-            // P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16, in fenced
-            // chunks beside the previous tile's deferred products
-            bf16x8 pb[2], dsb[2];
-            bf16x8 lop[3];
-            if constexpr (LATE) {
-                lop[0] = a_operand(at_prev, NEARLY);
-                lop[1] = a_operand(at_prev, NEARLY + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            constexpr int GPC = 16 / NLATE;   // registers per chunk
+            for (int qs = 0; qs < 2; ++qs)
     #pragma unroll
-            for (int i = 0; i < NLATE; ++i) {
-                if constexpr (LATE) late_mfma(at_prev, i, lop);
-    #pragma unroll
-                for (int g = GPC * i; g < GPC * (i + 1); ++g) {
-                    const float pg = __builtin_amdgcn_exp2f(fmaf(s[g], c2, -l2[g]));
-                    pb[g >> 3][g & 7] = static_cast<__bf16>(pg);
-                    dsb[g >> 3][g & 7] = static_cast<__bf16>(pg * dp[g]);
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(ls + 32 * qs + 16 * (rr >> 1) + 8 * hh + 4 * (rr & 1));
+                    l2v[qs][4 * rr + 0] = v4.x; l2v[qs][4 * rr + 1] = v4.y; l2v[qs][4 * rr + 2] = v4.z; l2v[qs][4 * rr + 3] = v4.w;
                 }
+            auto softmax = [&](int qs, const f32x16& sc, const f32x16& dp, int g0, int g1) {
+    #pragma unroll
+                for (int g = g0; g < g1; ++g) {
+                    const float l2 = l2v[qs][g];
+                    const float pg = __builtin_amdgcn_exp2f(fmaf(sc[g], c2, -l2));
+                    pb[qs][g >> 3][g & 7] = static_cast<__bf16>(pg);
+                    dsb[qs][g >> 3][g & 7] = static_cast<__bf16>(pg * dp[g]);
+                }
+            };
+            // dV^T and dK^T products of 16-query chunks c0, c0 + 1 (subtile
+            // c0 / 2): 4*DT products, A operands read two ahead
+            auto dvdk = [&](int c0, auto&& beside) {
+                constexpr int NP = 4 * DT;
+                auto asrc = [&](int n) {   // n: chunk c0 + (n / (2 DT)), tile dt, dO^T or Q^T
+                    const int c = c0 + n / (2 * DT), dt = (n >> 1) % DT;
+                    return ldtr((n & 1) ? qt : ot, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
+                };
+                bf16x8 op[3];
+                op[0] = asrc(0);
+                op[1] = asrc(1);
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            // stored transposed (row = key) for the products over the whole 64-query tile
     #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                *reinterpret_cast<bf16x8*>(ptbuf + pwo[c]) = pb[c];
-                *reinterpret_cast<bf16x8*>(ptbuf + pwo[c] + PT_BYTES) = dsb[c];
-            }
-            // Prefetch the next tile once this iteration's LDS stores are issued
-            // (LDS stores behind a pending direct-to-LDS load get made to wait).
-            // The deferred products above were the last readers of its buffer.
-            if (it + 1 < n_qt) copy_q(qt_base + BQ, std::integral_constant<int, buf ^ 1>{});
-            // P^T and dS^T of the whole tile are in LDS (LDS stores only: the
-            // prefetch just issued stays in flight across this barrier)
-            __builtin_amdgcn_s_waitcnt(kWaitLds);
-            __builtin_amdgcn_s_barrier();
-
-            // the first NEARLY products now; the B operands of the rest are read
-            // here too, as the next step overwrites the exchange buffer
-            const char* at = qh ? qt : ot;
-            bf16x8 op[3], bop = ld16(ptbuf, pto[0] + BO);
-            op[0] = a_operand(at, 0);
-            op[1] = a_operand(at, 1);
-    #pragma unroll
-            for (int i = 0; i < NLATE / DT; ++i) late_b[i] = ld16(ptbuf, pto[NEARLY / DT + i] + BO);
-            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-            for (int n = 0; n < NEARLY; ++n) {
-                if (n + 2 < NEARLY) op[(n + 2) % 3] = a_operand(at, n + 2);
-                const int c = n / DT, dt = n % DT;
-                const bf16x8 b = bop;
-                if (dt == DT - 1 && c + 1 < NEARLY / DT) bop = ld16(ptbuf, pto[c + 1] + BO);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], b, acc[dt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                for (int n = 0; n < NP; ++n) {
+                    if (n + 2 < NP) op[(n + 2) % 3] = asrc(n + 2);
+                    const int c = c0 + n / (2 * DT), dt = (n >> 1) % DT;
+                    if (n & 1)
+                        acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], dsb[c >> 1][c & 1], acck[dt], 0, 0, 0);
+                    else
+                        accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], pb[c >> 1][c & 1], accv[dt], 0, 0, 0);
+                    beside(n);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            f32x16 s0, dp0, s1, dp1;
+            sdp(0, s0, dp0, [](int) {});
+            mask(0, s0);
+            constexpr int G1 = 16 / (2 * KS);   // subtile-0 registers beside each S/dP product of subtile 1
+            sdp(1, s1, dp1, [&](int m) { softmax(0, s0, dp0, G1 * m, G1 * (m + 1)); });
+            mask(1, s1);
+            constexpr int G2 = 16 / (4 * DT);   // subtile-1 registers beside each dV/dK product of subtile 0
+            dvdk(0, [&](int n) { softmax(1, s1, dp1, G2 * n, G2 * (n + 1)); });
+            dvdk(2, [](int) {});
         };
-        // the deferred products of the last tile (buffer `bufc`)
-        auto flush = [&](auto bufc) {
+
+        if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
+        auto step = [&](int it, auto bufc) {
             constexpr int buf = decltype(bufc)::value;
-            const char* at = qh ? (buf ? qtile1 : qtile0) : (buf ? otile1 : otile0);
-            bf16x8 lop[3];
-            lop[0] = a_operand(at, NEARLY);
-            lop[1] = a_operand(at, NEARLY + 1);
-    #pragma unroll
-            for (int i = 0; i < NLATE; ++i) late_mfma(at, i, lop);
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();   // tile it is in LDS; every wave is done with tile it - 1
+            if (it + 1 < n_qt) copy_q((it + 1) * BQ, std::integral_constant<int, buf ^ 1>{});
+            tile(it, bufc);
         };
-        if (qt0 < n_qt) {
-            // the first tile has no deferred products before it
-            step(qt0, std::integral_constant<int, 0>{}, std::false_type{});
-            int it = qt0 + 1;
-            for (; it + 1 < n_qt; it += 2) {
-                step(it, std::integral_constant<int, 1>{}, std::true_type{});
-                step(it + 1, std::integral_constant<int, 0>{}, std::true_type{});
-            }
-            if (it < n_qt) {
-                step(it, std::integral_constant<int, 1>{}, std::true_type{});
-                flush(std::integral_constant<int, 1>{});
-            } else {
-                flush(std::integral_constant<int, 0>{});
-            }
+        for (int it = qt0; it < n_qt; it += 2) {
+            step(it, std::integral_constant<int, 0>{});
+            if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
         }
 
-        // ---- epilogue: dV (qh = 0) or dK = scale * (dK^T)^T (qh = 1), bf16 -------
+        // ---- epilogue: dV and dK = scale * (dK^T)^T, bf16 -------------------------
         // register g of lane half hh: column 32dt + 8(g>>2) + 4hh + (g&3) of key `key`
         if (key < a.N) {
-            u16* row = static_cast<u16*>(qh ? a.dk : a.dv) + base + int64_t(key) * a.ss;
-            const float f = qh ? a.scale : 1.0f;
+            u16* rv = static_cast<u16*>(a.dv) + base + int64_t(key) * a.ss;
+            u16* rk = static_cast<u16*>(a.dk) + base + int64_t(key) * a.ss;
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
     #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    __bf16 x4[4];
+                for (int rr = 0; rr < 4; ++rr) {
+                    __bf16 v4[4], k4[4];
     #pragma unroll
-                    for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * f);
-                    *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
+                    for (int t = 0; t < 4; ++t) {
+                        v4[t] = static_cast<__bf16>(accv[dt][4 * rr + t]);
+                        k4[t] = static_cast<__bf16>(acck[dt][4 * rr + t] * a.scale);
+                    }
+                    *reinterpret_cast<uint2*>(rv + 32 * dt + 8 * rr + 4 * hh) = __builtin_bit_cast(uint2, v4);
+                    *reinterpret_cast<uint2*>(rk + 32 * dt + 8 * rr + 4 * hh) = __builtin_bit_cast(uint2, k4);
                 }
         }
     }
@@ -684,8 +605,8 @@ int run(const BwdArgs& a, hipStream_t s) {
     if (err) return err;
     const int n_kt = (a.N + BK - 1) / BK;
     const unsigned g_kv = static_cast<unsigned>(int64_t(a.causal ? (n_kt + 1) / 2 : n_kt) * a.B * a.H);
-    if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(512), 0, s, a);
+    if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(256), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
