@@ -174,7 +174,7 @@ def cpu_baseline(w, target_s):
         if t_total >= target_s:
             break
     return {"value": done * flops_per_head / t_total / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "cpu": cpu_model(), "build": "gcc -O3 -march=native -fopenmp",
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "build": "gcc " + " ".join(oracle.NATIVE_CFLAGS),
             "kind": "oracle", "seconds": round(t_total, 3),
             "sample": f"{done} of {w.B * w.H} (batch, head) slices of the workload, every row, "
                       + ("fp64 analytic gradient, OpenMP over rows" if w.backward
@@ -184,7 +184,7 @@ def cpu_baseline(w, target_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(head sharding needs no communication; see the design notes). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

@@ -57,7 +57,7 @@ typedef enum flash_attn_status {
     FLASH_ATTN_ERR_SHAPE = 2,       /* a size is negative or beyond the limits below  */
     FLASH_ATTN_ERR_LAYOUT = 3,      /* strides / alignment not supported              */
     FLASH_ATTN_ERR_DTYPE = 4,       /* dtype not accepted by this entry point         */
-    FLASH_ATTN_ERR_UNSUPPORTED = 5, /* valid request this build does not implement    */
+    FLASH_ATTN_ERR_UNSUPPORTED = 5, /* valid request the library does not implement  */
     FLASH_ATTN_ERR_ARG = 6,         /* scale / option value out of range              */
     FLASH_ATTN_ERR_WORKSPACE = 7,   /* workspace missing or too small                 */
     FLASH_ATTN_ERR_HIP = 8          /* the HIP runtime reported an error              */

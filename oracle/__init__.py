@@ -54,6 +54,10 @@ _NATIVE = os.path.join(_HERE, "liboracle_native.so")
 _use_native = False
 
 
+# Flags of the host-tuned build that use_native_build() makes.
+NATIVE_CFLAGS = ("-O3", "-march=native", "-ffp-contract=off", "-fopenmp")
+
+
 def use_native_build() -> str:
     """Compile oracle.c for the host it runs on (gcc -O3 -march=native, FMA
     contraction off so the rounding is that of the plain build, no fast-math)
@@ -63,8 +67,7 @@ def use_native_build() -> str:
     if _lib is not None:
         raise RuntimeError("the oracle library is already loaded")
     tmp = _NATIVE + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", "-O3", "-march=native", "-ffp-contract=off", "-fopenmp", "-fPIC",
-                           "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"])
+    subprocess.check_call(["gcc", *NATIVE_CFLAGS, "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"])
     os.replace(tmp, _NATIVE)
     _use_native = True
     return _NATIVE
