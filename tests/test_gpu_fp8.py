@@ -129,7 +129,7 @@ def test_quantize_v_transposed_pow2(d, N):
     _check_codes(np.ascontiguousarray(c[:, :, :, :N].transpose(0, 1, 3, 2)), vref, osc, 64, vref)
 
 
-def _fp8_run(q, k, v, causal, d, signs, in_dtype="f32", q_terms=2):
+def _fp8_run(q, k, v, causal, d, signs, in_dtype="f32", q_terms=2, tau_log2=None):
     import exact_attention_77_amd as fa
     torch = _t()
     sdev = torch.from_numpy(signs).cuda()
@@ -139,7 +139,7 @@ def _fp8_run(q, k, v, causal, d, signs, in_dtype="f32", q_terms=2):
     q8, qs = fa.flash_attn_fp8_quantize(qd, fa.ROLE_Q, rotate=True, signs=sdev)
     k8, ks = fa.flash_attn_fp8_quantize(kd, fa.ROLE_K, rotate=True, signs=sdev)
     v8, vs = fa.flash_attn_fp8_quantize(vd, fa.ROLE_V)
-    o, lse = fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, q_terms=q_terms)
+    o, lse = fa.flash_attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, q_terms=q_terms, tau_log2=tau_log2)
     torch.cuda.synchronize()
     N = q.shape[2]
     q8c = q8.cpu().numpy()   # the code and its residual term (1/16)
@@ -228,6 +228,50 @@ def test_fp8_attention_accuracy(causal, d, N, q_terms):
     assert rmse <= 5e-2 and rmse < rmse_r1
     # the kernel against exact attention on its own dequantised inputs
     _check_kernel_only(o, lse, deq, causal)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1.0, 2.5, 8.0])
+def test_fp8_tau_forms_agree(tau):
+    """The fp8 kernel takes each tile's maximum first and moves the
+    reference when it exceeds the reference by more than tau, capped at 2.5
+    (64 * 2^2.5 < 448; the default 8 runs at the cap): classic online
+    softmax at 0, the cap at 2.5 and 8.  Every threshold gives exact
+    attention on the dequantised inputs within the bound of the e4m3
+    probabilities, and meets the accuracy bar."""
+    N, d = 900, 128
+    q, k, v = normal_qkv(1, 2, N, d, 91, outliers=True)
+    print(f"fp8 tau={tau} N={N} d={d}", flush=True)
+    for causal in (False, True):
+        o, lse, deq = _fp8_run(q, k, v, causal, d, hadamard_signs(d), tau_log2=tau)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        _check_kernel_only(o, lse, deq, causal)
+        o_ex, _ = oracle.attn_fwd(q, k, v, causal=causal)
+        assert float(np.sqrt(np.mean((o - o_ex) ** 2))) <= 5e-2
+
+
+@pytest.mark.parametrize("q_terms", [2, 1])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mag", [8.0, 12.0, 40.0, 400.0])
+def test_fp8_late_dominant_key(causal, mag, q_terms):
+    """Key 777 of 1000 aligns with every query (a shared component of 6 on
+    head dim 0, before the rotation), so its score stands above everything
+    before it: by about 1 (log2) with mag 8 (below the threshold), 4 with
+    mag 12 and 26 with mag 40 (both rescale; without it 64 p would overflow
+    e4m3), and about 300 with mag 400, where exp2 against the earlier
+    reference would leave the fp32 range."""
+    B, H, N, d = 1, 2, 1000, 128
+    q, k, v = normal_qkv(B, H, N, d, 83)
+    q[..., 0] += 6.0
+    k[:, :, 777, :] = 0.0
+    k[:, :, 777, 0] = mag
+    print(f"fp8 late dominant key mag={mag} causal={causal} q_terms={q_terms}", flush=True)
+    o, lse, deq = _fp8_run(q, k, v, causal, d, hadamard_signs(d), q_terms=q_terms)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    _check_kernel_only(o, lse, deq, causal)
+    if mag == 400.0:  # rows that see key 777 return V[777] up to the bf16 rounding of O
+        first = 777 if causal else 0
+        v777 = deq[2][0, :, 777]
+        assert np.max(np.abs(o[0, :, first:] - v777[:, None, :])) <= 2e-2
 
 
 def _fp8_full_size(q_terms=2):
