@@ -336,7 +336,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": ("synthetic (seeded N(0,1), 0.1% x20 outliers, fp32 -> e4m3 pre-pass)"
-                 if w.dtype == "fp8" else "synthetic (seeded N(0,1), bf16-rounded)"),
+                 if w.dtype == "fp8" else "synthetic (seeded N(0,1), bf16-rounded)" if w.dtype == "bf16"
+                 else "synthetic (seeded N(0,1), fp32)"),
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N,
                    "head_dim": w.d, "causal": w.causal, "scale": w.scale,
                    "flop_per_step": w.flops, "tile_cfg": args.tile_cfg},

@@ -85,9 +85,11 @@ typedef struct flash_attn_layout {
  *   rounding; unnormalised probabilities stay below 2^tau.  Range [0, 64];
  *   a negative value selects the default 8.
  * tile_cfg: 0 = automatic (bf16: 4-wave workgroups of 128 query rows for
- *   head_dim 64, 8-wave workgroups of 256 rows for 128); 1 and 2 force the
- *   8- and 4-wave forms of the bf16 kernel; any other value is an argument
- *   error.  The result does not depend on it beyond fp32 summation order.
+ *   head_dim 64, 8-wave workgroups of 256 rows for 128; f32: 8 waves unless
+ *   that grid has fewer than 512 workgroups, then 4); 1 and 2 force the 8-
+ *   and 4-wave forms of the bf16 and f32 kernels; any other value is an
+ *   argument error.  The result does not depend on it beyond fp32 summation
+ *   order.
  * fp8_q_terms: flash_attn_fwd_fp8 only (ignored elsewhere): 0 or 2 = use both
  *   e4m3 terms of Q (the default: Q K^T then carries only K's rounding), 1 =
  *   Q's first term only (four fewer fp8 products per 64-key tile at d = 128,

@@ -66,6 +66,8 @@ WORKLOADS = {
     "fp8_n8192_d128": Workload("fp8_n8192_d128", 2, 16, 8192, 128, "fp8", False, 3, outliers=True),
     "bf16_bwd_causal_n4096_d128": Workload("bf16_bwd_causal_n4096_d128", 2, 16, 4096, 128, "bf16",
                                            True, 4, backward=True),
+    # the fp32 path at a size that fills the chip (not one of the pages' configurations)
+    "f32_causal_n4096_d128": Workload("f32_causal_n4096_d128", 2, 16, 4096, 128, "f32", True, 6),
     # combine step of the headline shape sharded over 8 key ranges
     "merge_bf16_s8_n8192_d128": Workload("merge_bf16_s8_n8192_d128", 2, 16, 8192, 128, "bf16", False, 5,
                                          parts=8),
