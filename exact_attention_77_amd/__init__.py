@@ -313,17 +313,18 @@ def flash_attn_bwd_workspace_size(layout: Layout, dtype: int = DTYPE_BF16) -> in
 
 def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                    dq=None, dk=None, dv=None, workspace=None):
-    """Gradients (dq, dk, dv) of the bf16 forward for the upstream gradient dout.
+    """Gradients (dq, dk, dv) of the forward for the upstream gradient dout.
 
-    q, k, v, o, dout: bfloat16 CUDA tensors [B, H, N, d] sharing shape and
-    strides (o and lse are the forward's outputs); lse: float32 [B, H, N].
-    The fp32 workspace is allocated here unless given (uint8 tensor of at least
-    flash_attn_bwd_workspace_size bytes).
+    q, k, v, o, dout: bfloat16 or float32 CUDA tensors (one dtype for all)
+    [B, H, N, d] sharing shape and strides (o and lse are the forward's
+    outputs); lse: float32 [B, H, N].  The fp32 workspace is allocated here
+    unless given (uint8 tensor of at least flash_attn_bwd_workspace_size bytes).
     """
     import torch
     ts = (q, k, v, o, dout)
-    if any(t.dtype != torch.bfloat16 for t in ts):
-        raise FlashAttnError(4, "the backward takes bfloat16 q, k, v, o, dout")
+    if q.dtype not in (torch.bfloat16, torch.float32) or any(t.dtype != q.dtype for t in ts):
+        raise FlashAttnError(4, "the backward takes q, k, v, o, dout of one dtype, bfloat16 or float32")
+    dt_code = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F32
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):
         raise FlashAttnError(2, "q, k, v, o, dout must share a [B, H, N, d] shape")
     if any(t.stride() != q.stride() for t in ts):
@@ -342,14 +343,14 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | N
     outs = [t if t is not None else
             torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
             for t in (dq, dk, dv)]
-    need = flash_attn_bwd_workspace_size(lay, DTYPE_BF16)
+    need = flash_attn_bwd_workspace_size(lay, dt_code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d) if d else 1.0
     _check(load().flash_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                  lse.data_ptr(), dout.data_ptr(), outs[0].data_ptr(),
-                                 outs[1].data_ptr(), outs[2].data_ptr(), lay, DTYPE_BF16,
+                                 outs[1].data_ptr(), outs[2].data_ptr(), lay, dt_code,
                                  int(bool(causal)), float(scale), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream()))
     return tuple(outs)
@@ -362,8 +363,9 @@ def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool = Fal
     (B * H * N <= 2^21 rows).  Same arguments and result as flash_attn_bwd."""
     import torch
     ts = (q, k, v, o, dout, dq, dk, dv)
-    if any(t.dtype != torch.bfloat16 for t in ts):
-        raise FlashAttnError(4, "the backward takes bfloat16 tensors")
+    if q.dtype not in (torch.bfloat16, torch.float32) or any(t.dtype != q.dtype for t in ts):
+        raise FlashAttnError(4, "the backward takes tensors of one dtype, bfloat16 or float32")
+    dt_code = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F32
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):
         raise FlashAttnError(2, "q, k, v, o, dout, dq, dk, dv must share a [B, H, N, d] shape")
     if any(t.stride() != q.stride() for t in ts):
@@ -378,7 +380,7 @@ def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool = Fal
         scale = 1.0 / math.sqrt(d) if d else 1.0
     _check(load().flash_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                                         dk.data_ptr(), dv.data_ptr(), lay, DTYPE_BF16,
+                                         dk.data_ptr(), dv.data_ptr(), lay, dt_code,
                                          int(bool(causal)), float(scale), _stream()))
     return dq, dk, dv
 

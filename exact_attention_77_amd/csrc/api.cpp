@@ -223,7 +223,8 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
 }
 
 size_t flash_attn_bwd_workspace_size(flash_attn_layout layout, flash_attn_dtype dtype) {
-    if (check_shape(layout) != FLASH_ATTN_OK || dtype != FLASH_ATTN_BF16) return 0;
+    if (check_shape(layout) != FLASH_ATTN_OK || (dtype != FLASH_ATTN_BF16 && dtype != FLASH_ATTN_F32))
+        return 0;
     if (is_empty(layout)) return 0;
     return static_cast<size_t>(
         fa::bwd_workspace_bytes(layout.batch, layout.heads, layout.seqlen));
@@ -243,13 +244,12 @@ flash_attn_status bwd_impl(const void* q, const void* k, const void* v, const vo
                            bool from_scratch, void* stream) {
     flash_attn_status st = check_shape(layout);
     if (st != FLASH_ATTN_OK) return st;
-    if (dtype == FLASH_ATTN_F32) return FLASH_ATTN_ERR_UNSUPPORTED;
-    if (dtype != FLASH_ATTN_BF16) return FLASH_ATTN_ERR_DTYPE;
+    if (dtype != FLASH_ATTN_BF16 && dtype != FLASH_ATTN_F32) return FLASH_ATTN_ERR_DTYPE;
     if (causal != 0 && causal != 1) return FLASH_ATTN_ERR_ARG;
     if ((st = check_scale(scale)) != FLASH_ATTN_OK) return st;
     if (is_empty(layout)) return FLASH_ATTN_OK;
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FLASH_ATTN_ERR_NULL;
-    if ((st = check_strides(layout, 2)) != FLASH_ATTN_OK) return st;
+    if ((st = check_strides(layout, dtype == FLASH_ATTN_F32 ? 4 : 2)) != FLASH_ATTN_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u))
@@ -279,7 +279,7 @@ flash_attn_status bwd_impl(const void* q, const void* k, const void* v, const vo
     const int64_t rows = layout.batch * layout.heads * layout.seqlen;
     a.ws_lse2 = reinterpret_cast<float*>(ws);
     a.ws_nd = reinterpret_cast<float*>(ws + fa::bwd_ws_part(rows));
-    return hip_status(fa::launch_bwd_bf16(a, stream));
+    return hip_status(dtype == FLASH_ATTN_BF16 ? fa::launch_bwd_bf16(a, stream) : fa::launch_bwd_f32(a, stream));
 }
 
 }  // namespace

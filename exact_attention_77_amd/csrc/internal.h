@@ -52,8 +52,8 @@ struct Fp8Args {
     int32_t q_terms;       // 1: Q's first e4m3 term only; 2: both terms
 };
 
-// Backward arguments (bf16 tensors sharing one layout; fp32 workspace of two
-// per-row arrays [B, H, N]).
+// Backward arguments (bf16 or fp32 tensors sharing one layout; fp32 workspace
+// of two per-row arrays [B, H, N]).
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -103,6 +103,7 @@ int launch_fwd_f32(const FwdArgs& a, void* stream);
 int launch_fp8_quantize(const QuantArgs& a, void* stream);
 int launch_fwd_fp8(const Fp8Args& a, void* stream);
 int launch_bwd_bf16(const BwdArgs& a, void* stream);
+int launch_bwd_f32(const BwdArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 
 // Rows per scale block the fp8 attention kernel is built for (Q: a wave's

@@ -190,7 +190,7 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
                                      const flash_attn_fwd_opts* opts, void* stream);
 
 /*
- * Backward pass, bf16.  Gradients of the forward above with respect to Q, K
+ * Backward pass, bf16 or fp32.  Gradients of the forward above with respect to Q, K
  * and V for the upstream gradient dO.  The pages give no backward formulas;
  * this is the analytic derivative of the definition (s = scale Q K^T, P =
  * softmax(s) per row, P_ij = exp(s_ij - LSE_i)):
@@ -198,11 +198,12 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
  *     dQ = scale dS K,  dK = scale dS^T Q.
  * As in "FlashAttention: GPUメモリ階層を活用したアテンション最適化の分析"
  * sec. 7.2, S and P are recomputed tile by tile on chip from Q, K and the
- * forward's LSE; nothing N x N is stored.  Probabilities and dS enter the
- * matrix products as bf16, accumulation is fp32.
- *   q, k, v, o, dout : [layout] bf16 (o and lse are the forward's outputs)
+ * forward's LSE; nothing N x N is stored.  bf16: probabilities and dS enter
+ * the matrix products as bf16, accumulation is fp32; fp32: every product and
+ * sum is fp32.
+ *   q, k, v, o, dout : [layout] of `dtype` (o and lse are the forward's outputs)
  *   lse              : fp32 [batch, heads, seqlen] from flash_attn_fwd
- *   dq, dk, dv       : [layout] bf16 outputs (rounded to nearest even)
+ *   dq, dk, dv       : [layout] outputs of `dtype` (bf16: rounded to nearest even)
  *   causal, scale    : as given to the forward
  *   workspace        : device memory of at least
  *                      flash_attn_bwd_workspace_size(layout, dtype) bytes
@@ -211,7 +212,7 @@ flash_attn_status flash_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const
  *                      matter and are overwritten.
  * The result is deterministic: dK/dV are summed over query tiles and dQ over
  * key tiles inside one workgroup each, in a fixed order (no atomics).
- * Errors: as flash_attn_fwd; dtype F32 -> ERR_UNSUPPORTED (bf16 only);
+ * Errors: as flash_attn_fwd; a dtype other than BF16 or F32 -> ERR_DTYPE;
  * workspace NULL, too small or misaligned -> ERR_WORKSPACE.
  */
 flash_attn_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -181,7 +181,8 @@ def test_bwd_workspace_size():
     rows = 2 * 3 * 130
     part = lambda n: (4 * n + 255) // 256 * 256
     assert fa.flash_attn_bwd_workspace_size(lay) == 2 * part(rows)
-    assert fa.flash_attn_bwd_workspace_size(lay, fa.DTYPE_F32) == 0
+    assert fa.flash_attn_bwd_workspace_size(lay, fa.DTYPE_F32) == 2 * part(rows)
+    assert fa.flash_attn_bwd_workspace_size(lay, fa.DTYPE_FP8_E4M3) == 0
     assert fa.flash_attn_bwd_workspace_size(_lay(N=0)) == 0
     assert fa.flash_attn_bwd_workspace_size(_lay(d=96)) == 0
 
@@ -189,7 +190,12 @@ def test_bwd_workspace_size():
 def test_bwd_validation():
     for name in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"):
         assert bwd(**{name: None}) == 1, name
-    assert bwd(dtype=fa.DTYPE_F32) == 5
+    # fp32 is accepted: the same checks apply, with fp32 element strides
+    for name in ("q", "dout", "dv"):
+        assert bwd(dtype=fa.DTYPE_F32, **{name: None}) == 1, name
+    assert bwd(dtype=fa.DTYPE_F32, lay=_lay(ss=66)) == 3     # rows not 16-byte aligned
+    assert bwd(dtype=fa.DTYPE_F32, ws=None) == 7
+    assert bwd(dtype=fa.DTYPE_F32, dk=P + 4) == 3
     assert bwd(dtype=fa.DTYPE_FP8_E4M3) == 4
     assert bwd(causal=2) == 6
     assert bwd(scale=float("nan")) == 6
@@ -242,6 +248,7 @@ def test_bwd_noalloc_validation():
     assert bwd_noalloc(big) == 7                      # ERR_WORKSPACE, before any HIP call
     assert bwd_noalloc(_lay(N=0)) == 0
     assert bwd_noalloc(_lay(), q=None) == 1
-    assert bwd_noalloc(_lay(), dtype=fa.DTYPE_F32) == 5
+    assert bwd_noalloc(_lay(ss=66), dtype=fa.DTYPE_F32) == 3
+    assert bwd_noalloc(_lay(), dtype=fa.DTYPE_FP8_E4M3) == 4
     assert bwd_noalloc(_lay(ss=60)) == 3
     assert bwd_noalloc(_lay(), lse=P + 2) == 3

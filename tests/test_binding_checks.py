@@ -99,6 +99,18 @@ def test_bwd_rejects_host_tensors():
     assert _status(fa.flash_attn_bwd, q, k, v, q, lse, q) == ERR_ARG
 
 
+def test_bwd_dtypes():
+    """One dtype for every tensor, bfloat16 or float32; fp32 host tensors get
+    as far as the device check."""
+    q, k, v = _qkv()
+    qf, kf, vf = _qkv(dtype=torch.float32)
+    lse = torch.zeros((1, 2, 100))
+    assert _status(fa.flash_attn_bwd, qf, kf, vf, qf, lse, qf) == ERR_ARG
+    assert _status(fa.flash_attn_bwd, q, kf, v, q, lse, q) == ERR_DTYPE
+    assert _status(fa.flash_attn_bwd, q.half(), k.half(), v.half(), q.half(), lse, q.half()) == ERR_DTYPE
+    assert _status(fa.flash_attn_bwd_noalloc, qf, kf, vf, qf, lse, qf, qf, kf, q) == ERR_DTYPE
+
+
 def test_merge_rejects_out_of_another_shape():
     parts = torch.zeros((3, 2, 2, 50, 64), dtype=torch.bfloat16)
     lse = torch.zeros((3, 2, 2, 50))

@@ -31,10 +31,14 @@ def _torch():
     return torch
 
 
-def _inputs(B, H, N, d, seed, layout="bhnd"):
+def _inputs(B, H, N, d, seed, layout="bhnd", dtype="bf16"):
     torch = _torch()
     xs = normal_qkv(B, H, N, d, seed, with_dout=True)
-    tens, ref = zip(*(to_bf16(x) for x in xs))
+    if dtype == "bf16":
+        tens, ref = zip(*(to_bf16(x) for x in xs))
+    else:
+        tens = [torch.from_numpy(x) for x in xs]
+        ref = [x.astype(np.float64) for x in xs]
     if layout == "bnhd":  # [B, N, H, d] storage viewed as [B, H, N, d]
         dev = [t.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3) for t in tens]
     else:
@@ -82,6 +86,63 @@ def _check_full(grads, ref, causal, report=print):
         report(f"{name}: rms err {rms_gpu:.3e} vs bf16 standard attention {rms_base:.3e} "
                f"(ratio {rms_gpu / max(rms_base, 1e-30):.2f}, bound 2)")
         assert rms_gpu <= 2.0 * rms_base + 1e-4 * max(rms_ref, RMS_FLOOR), name
+
+
+# fp32: every product and sum is fp32 (relative rounding 2^-24 per step).  The
+# gradients sum up to N terms of products that are each within a few fp32
+# roundings of the exact ones, so their error is bounded by a small multiple
+# of 2^-24 * sqrt(N) * (the row's magnitude); with N <= 4096 we require
+# max|err| <= 1e-4 * max(1, max|ref|) and RMS error <= 1e-5 * max(RMS(ref),
+# 0.1), two decades above the measured errors and three below the bf16 bound.
+# The floor: dP - D is the difference of two fp32 dot products of size about
+# |dO| |V| ~ 1 here, so a gradient that is exactly 0 (one key) still comes out
+# at a few 1e-7.
+F32_ABS_TOL = 1e-4
+F32_RMS_TOL = 1e-5
+F32_RMS_FLOOR = 0.1
+
+
+def _check_f32(grads, ref, causal, report=print):
+    exact = oracle.attn_bwd(*ref, causal=causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, exact):
+        assert g.shape == r.shape and np.all(np.isfinite(g)), name
+        err = np.abs(g - r)
+        bound = F32_ABS_TOL * max(1.0, float(np.max(np.abs(r))) if r.size else 1.0)
+        rms_ref = float(np.sqrt(np.mean(r ** 2))) if r.size else 0.0
+        rms_err = float(np.sqrt(np.mean(err ** 2))) if r.size else 0.0
+        report(f"{name} fp32: max|err|={err.max() if err.size else 0:.3e} (bound {bound:.3e}) "
+               f"rms err/ref={rms_err / max(rms_ref, 1e-30):.3e}")
+        assert err.size == 0 or float(err.max()) <= bound, name
+        assert rms_err <= F32_RMS_TOL * max(rms_ref, F32_RMS_FLOOR), name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 64, 130, 255, 600])
+def test_bwd_f32_parity(N, d, causal):
+    print(f"bwd fp32 N={N} d={d} causal={causal}", flush=True)
+    dev, ref = _inputs(1, 2, N, d, 2100 + N + d, dtype="f32")
+    _check_f32(_fwd_bwd(dev, causal), ref, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f32_layouts_and_repeat(causal):
+    """[B, N, H, d] storage, several heads and batches, and a bitwise repeat."""
+    dev, ref = _inputs(2, 3, 190, 128, 33, layout="bnhd", dtype="f32")
+    a = _fwd_bwd(dev, causal)
+    b = _fwd_bwd(dev, causal)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    _check_f32(a, ref, causal)
+
+
+def test_bwd_f32_full_size_all_rows(margin):
+    """The backward workload's shape in fp32 (B=2, H=16, N=4096, d=128,
+    causal): every row of dQ, dK and dV against the oracle."""
+    w = WORKLOADS["bf16_bwd_causal_n4096_d128"]
+    print(f"bwd fp32 full size {w.B}x{w.H}x{w.N}x{w.d}", flush=True)
+    dev, ref = _inputs(w.B, w.H, w.N, w.d, w.seed, dtype="f32")
+    _check_f32(_fwd_bwd(dev, w.causal), ref, w.causal, lambda line: margin(f"bwd fp32 B2 H16 N4096 d128 all rows {line}"))
 
 
 @pytest.mark.parametrize("causal", [False, True])
