@@ -166,7 +166,8 @@ def cpu_baseline(w, target_s):
             ref = [x[b:b + 1, h:h + 1] for x in (q, k, v)]
         t0 = time.perf_counter()
         if w.backward:
-            oracle.attn_bwd(*ref, to_bf16(dout[b:b + 1, h:h + 1])[1], causal=w.causal)
+            d1 = dout[b:b + 1, h:h + 1]
+            oracle.attn_bwd(*ref, to_bf16(d1)[1] if w.dtype == "bf16" else d1, causal=w.causal)
         else:
             oracle.attn_fwd(*ref, causal=w.causal)
         t_total += time.perf_counter() - t0
@@ -202,7 +203,7 @@ def main():
         return bench_merge(args, w, dev)
     if w.backward:
         q, k, v, dout = normal_qkv(w.B, w.H, w.N, w.d, w.seed, with_dout=True)
-        dout = to_bf16(dout)[0].to(dev)
+        dout = (to_bf16(dout)[0] if w.dtype == "bf16" else torch.from_numpy(dout)).to(dev)
     else:
         q, k, v = normal_qkv(w.B, w.H, w.N, w.d, w.seed, outliers=w.outliers)
     extra = {}
@@ -266,7 +267,8 @@ def main():
         fa.flash_attn_fwd(*tens, causal=w.causal, scale=w.scale, out=o, lse=lse)
         grads = [torch.empty_like(tens[0]) for _ in range(3)]
         lay = fa.Layout(w.B, w.H, w.N, w.d, *tens[0].stride()[:3])
-        ws = torch.empty(fa.flash_attn_bwd_workspace_size(lay), dtype=torch.uint8, device=dev)
+        ws = torch.empty(fa.flash_attn_bwd_workspace_size(lay, fa.DTYPE_BF16 if w.dtype == "bf16" else fa.DTYPE_F32),
+                         dtype=torch.uint8, device=dev)
 
     def step():
         if w.backward:

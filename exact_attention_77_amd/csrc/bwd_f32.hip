@@ -171,10 +171,17 @@ void bwd_f32_dq_kernel(BwdArgs a) {
             f32x16 s, dp;
     #pragma unroll
             for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = nd; }
+            // the chunks of read u + 1 are issued before the products of read u
+            float4 kn = *reinterpret_cast<const float4*>(kl + TL::chunk_off(j, hh));
+            float4 vn = *reinterpret_cast<const float4*>(vl + TL::chunk_off(j, hh));
+            __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
             for (int u = 0; u < KU; ++u) {
-                const float4 kx = *reinterpret_cast<const float4*>(kl + TL::chunk_off(j, 2 * u + hh));
-                const float4 vx = *reinterpret_cast<const float4*>(vl + TL::chunk_off(j, 2 * u + hh));
+                const float4 kx = kn, vx = vn;
+                if (u + 1 < KU) {
+                    kn = *reinterpret_cast<const float4*>(kl + TL::chunk_off(j, 2 * u + 2 + hh));
+                    vn = *reinterpret_cast<const float4*>(vl + TL::chunk_off(j, 2 * u + 2 + hh));
+                }
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qreg[4 * u + 0], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vx.x, oreg[4 * u + 0], dp, 0, 0, 0);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qreg[4 * u + 1], s, 0, 0, 0);
@@ -183,6 +190,7 @@ void bwd_f32_dq_kernel(BwdArgs a) {
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vx.z, oreg[4 * u + 2], dp, 0, 0, 0);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qreg[4 * u + 3], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vx.w, oreg[4 * u + 3], dp, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             const int k0 = kt * BT;
             if ((k0 + BT > a.N) || (CAUSAL && k0 + BT - 1 > q0)) {   // wave-uniform
@@ -194,15 +202,24 @@ void bwd_f32_dq_kernel(BwdArgs a) {
             // dS^T = P^T o (dP^T - D), in place of the scores
     #pragma unroll
             for (int g = 0; g < 16; ++g) s[g] = __builtin_amdgcn_exp2f(fmaf(s[g], c2, -lse2)) * dp[g];
-            // dQ^T += K^T dS^T: product t takes the key pair of register t
-    #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            // dQ^T += K^T dS^T: product n takes the key pair of register n / DT
+            // (head-dim tile n % DT); its K^T operand is read PF products ahead
+            constexpr int NP = 16 * DT, PF = 4;
+            auto ksrc = [&](int n) {
+                const int t = n / DT, dt = n % DT;
                 const int row = 8 * (t >> 2) + 4 * hh + (t & 3);
+                return *reinterpret_cast<const float*>(kl + TL::float_off(row, 32 * dt + j));
+            };
+            float kb[PF];
     #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const float kv = *reinterpret_cast<const float*>(kl + TL::float_off(row, 32 * dt + j));
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, s[t], acc[dt], 0, 0, 0);
-                }
+            for (int n = 0; n < PF; ++n) kb[n] = ksrc(n);
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int n = 0; n < NP; ++n) {
+                const float kv = kb[n % PF];
+                if (n + PF < NP) kb[n % PF] = ksrc(n + PF);
+                acc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, s[n / DT], acc[n % DT], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
@@ -326,10 +343,17 @@ void bwd_f32_dkdv_kernel(BwdArgs a) {
             f32x16 s, dp;
     #pragma unroll
             for (int g = 0; g < 16; ++g) { s[g] = 0.f; dp[g] = ndv[g]; }
+            // the chunks of read u + 1 are issued before the products of read u
+            float4 qn = *reinterpret_cast<const float4*>(ql + TL::chunk_off(j, hh));
+            float4 on = *reinterpret_cast<const float4*>(ol + TL::chunk_off(j, hh));
+            __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
             for (int u = 0; u < KU; ++u) {
-                const float4 qx = *reinterpret_cast<const float4*>(ql + TL::chunk_off(j, 2 * u + hh));
-                const float4 ox = *reinterpret_cast<const float4*>(ol + TL::chunk_off(j, 2 * u + hh));
+                const float4 qx = qn, ox = on;
+                if (u + 1 < KU) {
+                    qn = *reinterpret_cast<const float4*>(ql + TL::chunk_off(j, 2 * u + 2 + hh));
+                    on = *reinterpret_cast<const float4*>(ol + TL::chunk_off(j, 2 * u + 2 + hh));
+                }
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(qx.x, kreg[4 * u + 0], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ox.x, vreg[4 * u + 0], dp, 0, 0, 0);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(qx.y, kreg[4 * u + 1], s, 0, 0, 0);
@@ -338,6 +362,7 @@ void bwd_f32_dkdv_kernel(BwdArgs a) {
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ox.z, vreg[4 * u + 2], dp, 0, 0, 0);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(qx.w, kreg[4 * u + 3], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ox.w, vreg[4 * u + 3], dp, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // masked (query, key) pairs: queries past the end, and under the
             // causal mask queries before the key, get P = 0
@@ -356,17 +381,26 @@ void bwd_f32_dkdv_kernel(BwdArgs a) {
                 s[g] = __builtin_amdgcn_exp2f(fmaf(s[g], c2, -l2[g]));   // P
                 ds[g] = s[g] * dp[g];                                   // dS
             }
-            // dV^T += dO^T P and dK^T += Q^T dS: product t takes the query pair of register t
-    #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            // dV^T += dO^T P and dK^T += Q^T dS: product pair n takes the query
+            // pair of register n / DT (head-dim tile n % DT); the dO^T and Q^T
+            // operands are read PF pairs ahead
+            constexpr int NP = 16 * DT, PF = 3;
+            auto src = [&](const char* t_lds, int n) {
+                const int t = n / DT, dt = n % DT;
                 const int row = 8 * (t >> 2) + 4 * hh + (t & 3);
+                return *reinterpret_cast<const float*>(t_lds + TL::float_off(row, 32 * dt + j));
+            };
+            float ob[PF], qb[PF];
     #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const float ov = *reinterpret_cast<const float*>(ol + TL::float_off(row, 32 * dt + j));
-                    const float qv = *reinterpret_cast<const float*>(ql + TL::float_off(row, 32 * dt + j));
-                    accv[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ov, s[t], accv[dt], 0, 0, 0);
-                    acck[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv, ds[t], acck[dt], 0, 0, 0);
-                }
+            for (int n = 0; n < PF; ++n) { ob[n] = src(ol, n); qb[n] = src(ql, n); }
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int n = 0; n < NP; ++n) {
+                const float ov = ob[n % PF], qv = qb[n % PF];
+                if (n + PF < NP) { ob[n % PF] = src(ol, n + PF); qb[n % PF] = src(ql, n + PF); }
+                accv[n % DT] = __builtin_amdgcn_mfma_f32_32x32x2f32(ov, s[n / DT], accv[n % DT], 0, 0, 0);
+                acck[n % DT] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv, ds[n / DT], acck[n % DT], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 

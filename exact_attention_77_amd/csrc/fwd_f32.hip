@@ -132,14 +132,18 @@ __device__ __forceinline__ void f32_tile(const FwdArgs& a, char* lds, int bh, in
     auto tile = [&](int kt, const char* kt_lds, const char* vt_lds) {
         const float* krow = reinterpret_cast<const float*>(kt_lds + j * (D * 4));
         f32x16 se = {}, so = {};
+        // the chunk of read u + 1 is issued before the products of read u
+        float4 kn = *reinterpret_cast<const float4*>(krow + 4 * (hh ^ TL::kswz(j)));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < D / 8; ++u) {
-            const int ch = (2 * u + hh) ^ TL::kswz(j);
-            const float4 kx = *reinterpret_cast<const float4*>(krow + 4 * ch);
+            const float4 kx = kn;
+            if (u + 1 < D / 8) kn = *reinterpret_cast<const float4*>(krow + 4 * ((2 * u + 2 + hh) ^ TL::kswz(j)));
             se = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qreg[4 * u + 0], se, 0, 0, 0);
             so = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qreg[4 * u + 1], so, 0, 0, 0);
             se = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.z, qreg[4 * u + 2], se, 0, 0, 0);
             so = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qreg[4 * u + 3], so, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         f32x16 s = se + so;
         // keys past the query (causal) or past the end score -inf; register g
@@ -170,15 +174,25 @@ __device__ __forceinline__ void f32_tile(const FwdArgs& a, char* lds, int bh, in
             s[g] = __builtin_amdgcn_exp2f(fmaf(s[g], c2, -m_ref));
             lpart += s[g];
         }
-        // PV: product t takes the key pair of register t, keys
-        // 8 (t / 4) + 4 hh + t % 4 in lane half hh
+        // PV: product n takes the key pair of register t = n / DT (keys
+        // 8 (t / 4) + 4 hh + t % 4 in lane half hh) and head-dim tile n % DT;
+        // its V operand is read PF products ahead
         const float* vbase = reinterpret_cast<const float*>(vt_lds) + j;
+        constexpr int NP = 16 * DT, PF = 4;
+        auto vsrc = [&](int n) {
+            const int t = n / DT, dt = n % DT;
+            return vbase[(8 * (t >> 2) + 4 * hh + (t & 3)) * D + 32 * dt];
+        };
+        float vb[PF];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const float* vrow = vbase + (8 * (t >> 2) + 4 * hh + (t & 3)) * D;
+        for (int n = 0; n < PF; ++n) vb[n] = vsrc(n);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * dt], s[t], oacc[dt], 0, 0, 0);
+        for (int n = 0; n < NP; ++n) {
+            const float vv = vb[n % PF];
+            if (n + PF < NP) vb[n % PF] = vsrc(n + PF);
+            oacc[n % DT] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s[n / DT], oacc[n % DT], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

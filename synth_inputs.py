@@ -68,6 +68,8 @@ WORKLOADS = {
                                            True, 4, backward=True),
     # the fp32 path at a size that fills the chip (not one of the pages' configurations)
     "f32_causal_n4096_d128": Workload("f32_causal_n4096_d128", 2, 16, 4096, 128, "f32", True, 6),
+    "f32_bwd_causal_n4096_d128": Workload("f32_bwd_causal_n4096_d128", 2, 16, 4096, 128, "f32",
+                                          True, 7, backward=True),
     # combine step of the headline shape sharded over 8 key ranges
     "merge_bf16_s8_n8192_d128": Workload("merge_bf16_s8_n8192_d128", 2, 16, 8192, 128, "bf16", False, 5,
                                          parts=8),
