@@ -64,6 +64,8 @@ WORKLOADS = {
     "bf16_n2048_d64": Workload("bf16_n2048_d64", 4, 16, 2048, 64, "bf16", False, 1),
     "bf16_causal_n8192_d128": Workload("bf16_causal_n8192_d128", 2, 16, 8192, 128, "bf16", True, 2),
     "fp8_n8192_d128": Workload("fp8_n8192_d128", 2, 16, 8192, 128, "fp8", False, 3, outliers=True),
+    # the fp8 path under the causal mask (not one of the pages' configurations)
+    "fp8_causal_n8192_d128": Workload("fp8_causal_n8192_d128", 2, 16, 8192, 128, "fp8", True, 8, outliers=True),
     "bf16_bwd_causal_n4096_d128": Workload("bf16_bwd_causal_n4096_d128", 2, 16, 4096, 128, "bf16",
                                            True, 4, backward=True),
     # the fp32 path at a size that fills the chip (not one of the pages' configurations)
