@@ -1,7 +1,7 @@
 """Throughput over sequence length on one GPU, on the grid the
 "FlashAttention-3" page benchmarks (実験設定): batch x seqlen = 16k tokens,
-16 heads, head_dim 64 and 128, N = 512 .. 16k, with and without the causal
-mask.  bf16 forward and backward, and (d = 128) the fp8 forward on the
+N = 512 .. 16k, with and without the causal mask, head_dim 64 and 128; the
+head count (16 by default) is not given there.  bf16 forward and backward, and (d = 128) the fp8 forward on the
 pre-pass outputs.  Seeded random inputs already in HBM; each point is the best
 of three batches of 20 back-to-back launches after a settle phase of 200
 headline-shaped launches.  Prints one JSON object per point.
