@@ -1,7 +1,9 @@
 """The library used from C alone: tests/c_api/abi_consumer (built by the
-package build) runs one causal bf16 forward through include/flash_attn.h on
-HIP device buffers, checks it against the fp64 oracle (max |dO| <= 2e-2,
-max |dLSE| <= 1e-2) and two synchronous error returns."""
+package build) runs one causal bf16 forward and its backward through
+include/flash_attn.h on HIP device buffers, checks both against the fp64
+oracle (O within 2e-2, LSE within 1e-2; each gradient within
+2e-2 * max(1, max |g_ref|) and an RMS error of 1e-2 of its RMS) and three
+synchronous error returns."""
 import os
 import subprocess
 
