@@ -68,6 +68,9 @@ typedef __attribute__((address_space(1))) const void global_cvoid;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BC = 64;  // keys per K/V tile
+// s_waitcnt immediate that waits for LDS (and scalar memory) operations only:
+// vmcnt and expcnt at their maxima, lgkmcnt 0.
+constexpr int kLgkm0 = 0xC07F;
 constexpr int WQ = 32;  // query rows per wave
 constexpr bf16x2 kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
@@ -95,7 +98,9 @@ template <int D>
 struct Tile {
     static constexpr int CPR = D / 8;               // 16-byte chunks per row
     static constexpr int BYTES = BC * D * 2;        // one K or V tile
-    static constexpr int LDS_BYTES = 4 * BYTES;     // K0 K1 V0 V1
+    static constexpr int QS_OFF = 4 * BYTES;        // K0 K1 V0 V1, then the waves' Q/O slices
+    static constexpr int SLICE = 32 * D * 2;        // one wave's 32 rows of Q or O
+    static constexpr int lds_bytes(int nw) { return QS_OFF + nw * SLICE; }
     // XOR swizzles (in 16-byte chunk units) applied to a row's chunk index.
     // K: 16 lanes read one logical chunk of 16 different rows.
     __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
@@ -129,9 +134,16 @@ __device__ __forceinline__ short4_t lds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((__attribute__((address_space(3))) char*)(p)));
 }
 
-// One 256-query tile (NW waves of 32 queries) of head bh.
+// One 256-query tile (NW waves of 32 queries) of head bh.  With `issued` the
+// tile's Q rows (in the waves' LDS slices) and its first K/V tiles were
+// copied by the previous call, which also waited for them and passed a
+// barrier.  With next_qt >= 0 the tile ends by starting the K/V copies of
+// query tile next_qt of the same head before it normalises and stores its
+// own O, then copies the next Q rows into the slices the O rows have left:
+// the next tile's loads overlap this tile's epilogue.
 template <int D, int NW, bool CAUSAL>
-__device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int bh, int qt) {
+__device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int bh, int qt, int next_qt,
+                                              bool issued) {
     using TL = Tile<D>;
     constexpr int BR = NW * WQ;                       // query rows per workgroup
     constexpr int KSTEPS = D / 16;
@@ -154,7 +166,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     const int qi = q0 + j;               // this lane's query row
 
     const int n_kt_all = (a.N + BC - 1) / BC;
-    const int nt = CAUSAL ? min(n_kt_all, (min(a.N, (qt + 1) * BR) + BC - 1) / BC) : n_kt_all;
+    auto n_ktiles = [&](int t) { return CAUSAL ? min(n_kt_all, (min(a.N, (t + 1) * BR) + BC - 1) / BC) : n_kt_all; };
+    const int nt = n_ktiles(qt);
     int wnt = CAUSAL ? min(nt, (min(a.N, q0 + WQ) + BC - 1) / BC) : nt;
     if (q0 >= a.N) wnt = 0;
 
@@ -194,14 +207,41 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     };
     constexpr int K_OFF0 = 0, K_OFF1 = TL::BYTES, V_OFF0 = 2 * TL::BYTES, V_OFF1 = 3 * TL::BYTES;
 
-    // ---- Q^T operand: lane (query j, half hh) holds Q[qi][16ks + 8hh .. +7] ----
-    bf16x8 qreg[KSTEPS];
+    // ---- Q in and O out through the wave's own LDS slice (32 rows x D) -------
+    // Global memory sees whole rows: Q is copied in 1 KB blocks (lane L of
+    // block i fills slice chunk 64 i + L: row (64 i + L) / CPR, physical chunk
+    // (64 i + L) % CPR holding logical chunk physical ^ kswz(row)), and O
+    // leaves 16 bytes of a row per lane.  Only the registers see the
+    // transposed layout (one query per lane).  A wave touches only its own
+    // slice, so the slice needs no workgroup barrier.  Rows past the end copy
+    // the last row (never stored).
+    constexpr int NQ = TL::SLICE / 1024;              // 1 KB copies per slice
+    constexpr int RPI = 64 / TL::CPR;                 // rows per 16-byte-per-lane access
+    char* const qs = smem + TL::QS_OFF + wave * TL::SLICE;
+    // The slice addressing is recomputed at each use from an opaque copy of
+    // the lane index: shared with the tile's other end it would stay live
+    // across the main loop and cost registers there.
+    auto fresh_lane = [&]() {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    auto copy_q = [&](int t) {
+        const int r0 = t * BR + wave * WQ, l = fresh_lane();
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (qi < a.N) x = *reinterpret_cast<const uint4*>(Qg + int64_t(qi) * a.ss + 16 * ks + 8 * hh);
-        qreg[ks] = __builtin_bit_cast(bf16x8, x);
-    }
+        for (int i = 0; i < NQ; ++i) {
+            const int c = i * 64 + l, row = c / TL::CPR, pch = c % TL::CPR;
+            copy16_to_lds(Qg + int64_t(min(r0 + row, a.N - 1)) * a.ss + 8 * (pch ^ TL::kswz(row)), qs + i * 1024);
+        }
+    };
+    // Q^T operand: lane (query j, half hh) holds Q[qi][16ks + 8hh .. +7]
+    bf16x8 qreg[KSTEPS];
+    auto read_q = [&]() {
+        const int l = fresh_lane(), jj = l & 31, h2 = l >> 5;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            qreg[ks] = *reinterpret_cast<const bf16x8*>(qs + jj * (2 * D) + 16 * ((2 * ks + h2) ^ TL::kswz(jj)));
+    };
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -408,14 +448,21 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         for (int i = 0; i < NDEF; ++i) vdef[i] = vb[(PVM - NDEF + i) % NPV];
     };
 
-    // ---- prologue: K0, V0, K1 in flight; S(0) ---------------------------------
-    if (nt > 0) {
-        copy_tile(kp, 0, K_OFF0);
-        copy_tile(vp, 0, V_OFF0);
+    // ---- prologue: Q^T, K0, V0, K1 in flight; S(0) -----------------------------
+    auto first_copies = [&](int n) {
+        if (n > 0) {
+            copy_tile(kp, 0, K_OFF0);
+            copy_tile(vp, 0, V_OFF0);
+        }
+        if (n > 1) copy_tile(kp, 1, K_OFF1);
+    };
+    if (!issued) {
+        copy_q(qt);
+        first_copies(nt);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
-    if (nt > 1) copy_tile(kp, 1, K_OFF1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    read_q();
 
     f32x16 sA[2], sB[2];
     if (wnt > 0) {
@@ -423,7 +470,10 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         if (needs_mask(0)) apply_mask(sA, 0);
         m_ref = tile_max(sA) * c2;  // finite: key 0 is allowed for every query
     }
-    __syncthreads();  // every wave is done with K0 before K2 overwrites it
+    // every wave is done with K0 before K2 overwrites it (LDS reads only: the
+    // previous tile's O stores need not have completed)
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
 
     // ---- main loop, unrolled by two so buffers and score sets alternate ------
     auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
@@ -444,21 +494,47 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
 
     flush_deferred();
 
+    // ---- handover: the next tile's K/V copies go out first ------------------
+    // The loop's last barrier came after every wave's last LDS read, so the
+    // buffers are free for the next tile's copies.
+    if (next_qt >= 0) first_copies(n_ktiles(next_qt));
+
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
-    if (qi < a.N && wnt > 0) {
-        const float lt = kRowsumMfma ? lsum : pair_sum(lsum);
-        const float inv = 1.0f / lt;
-        u16* orow = Og + int64_t(qi) * a.ss;
+    // O^T into the slice (row j, logical chunk 4 dt + r, half hh), then back as
+    // whole rows: lane L holds row RPI i + L / CPR, physical chunk L % CPR.
+    const float lt = kRowsumMfma ? lsum : pair_sum(lsum);
+    const float inv = 1.0f / lt;
+    const int le = fresh_lane();
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                __bf16 o4[4];
+        for (int r = 0; r < 4; ++r) {
+            __bf16 o4[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * r + t] * inv);
-                *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, o4);
-            }
-        if (hh == 0) a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt)) * 0.69314718055994531f;
+            for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * r + t] * inv);
+            const int jj = le & 31, h2 = le >> 5;
+            *reinterpret_cast<uint2*>(qs + jj * (2 * D) + 16 * ((4 * dt + r) ^ TL::kswz(jj)) + 8 * h2) =
+                __builtin_bit_cast(uint2, o4);
+        }
+    if (wnt > 0) {
+#pragma unroll
+        for (int i = 0; i < WQ / RPI; ++i) {
+            const int row = RPI * i + le / TL::CPR;
+            const uint4 orow = *reinterpret_cast<const uint4*>(qs + row * (2 * D) + 16 * (le % TL::CPR));
+            if (q0 + row < a.N)
+                *reinterpret_cast<uint4*>(Og + int64_t(q0 + row) * a.ss +
+                                          8 * ((le % TL::CPR) ^ TL::kswz(row))) = orow;
+        }
+        if (qi < a.N && hh == 0) a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt)) * 0.69314718055994531f;
+    }
+    // The next tile's Q rows go into the slice once this wave's O rows are
+    // out of it; its copies were issued after the O stores, so the wait for
+    // them costs little beyond their own latency.
+    if (next_qt >= 0) {
+        __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's O rows are out of its slice
+        copy_q(next_qt);
+        __builtin_amdgcn_s_waitcnt(0);        // the next tile's copies have landed
+        __builtin_amdgcn_s_barrier();         // ... in every wave
     }
 }
 
@@ -486,16 +562,14 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int hi = CAUSAL ? n_qt - 1 - p : p;
     const int n_tiles = (CAUSAL && p < hi) ? 2 : 1;
 #pragma nounroll
-    for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
-        if (r) __syncthreads();           // every wave is done with the first tile's LDS buffers
-        fwd_bf16_tile<D, NW, CAUSAL>(a, smem, bh, r ? p : hi);
-    }
+    for (int r = 0; r < n_tiles; ++r)     // one copy of the tile code
+        fwd_bf16_tile<D, NW, CAUSAL>(a, smem, bh, r ? p : hi, r + 1 < n_tiles ? p : -1, r > 0);
 }
 
 template <int D, int NW, bool CAUSAL>
 int launch(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = NW * WQ;
-    constexpr int LDS = Tile<D>::LDS_BYTES;
+    constexpr int LDS = Tile<D>::lds_bytes(NW);
     auto kern = fwd_bf16_kernel<D, NW, CAUSAL>;
     // set once per process (thread-safe initialisation of a local static)
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
