@@ -82,9 +82,9 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantArgs a) {
     const int blk_rows = (a.role == 0) ? kQBlk : (a.role == 1) ? kKBlk : kVBlk;
     const int nblk = (a.N + blk_rows - 1) / blk_rows;
     const int nwg = (a.N + RWG - 1) / RWG;
-    const int bh = blockIdx.x / nwg, g = blockIdx.x % nwg;
+    const int bh = __builtin_amdgcn_workgroup_id_x() / nwg, g = __builtin_amdgcn_workgroup_id_x() % nwg;
     const int b = bh / a.H, h = bh % a.H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR;                    // columns 32c .. 32c+31
     const int rw = wave * RPW + lane / LPR;      // row inside the workgroup
     const int row = g * RWG + rw;
@@ -238,6 +238,9 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int BC = kVBlk;   // keys per tile
+// s_waitcnt immediate that waits for LDS (and scalar memory) operations only:
+// vmcnt and expcnt at their maxima, lgkmcnt 0.
+constexpr int kLgkm0 = 0xC07F;
 constexpr int WQ = 32;      // query rows per wave
 
 template <int D>
@@ -252,6 +255,13 @@ struct Tile8 {
     }
     // V^T: 16 consecutive head-dim rows of 64 bytes.
     __device__ static int vswz(int r) { return (r >> 2) & 3; }
+    // A wave's slice: its 32 Q rows (both e4m3 planes, D bytes each) on the
+    // way in, its 32 bf16 O rows on the way out.
+    static constexpr int SLICE = 32 * D * 2;
+    // Q rows of D bytes: lanes of one half-wave read one chunk of 16 rows.
+    __device__ static int qswz(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+    // O rows of 2 D bytes (the bf16 kernel's K-row swizzle).
+    __device__ static int oswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 // A-operand row rho of score subtile st loads key
@@ -299,13 +309,14 @@ void fwd_fp8_kernel(Fp8Args a) {
     __shared__ __attribute__((aligned(1024))) char lds_k1[TL::KBYTES];
     __shared__ __attribute__((aligned(1024))) char lds_v0[TL::VBYTES];
     __shared__ __attribute__((aligned(1024))) char lds_v1[TL::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_qo[NW * TL::SLICE];
 
     // One head per XCD; under the causal mask a workgroup takes the query-tile
     // pair (T-1-p, p), so that all workgroups carry the same work.
     const int n_qt = (a.N + BR - 1) / BR;
     const int per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
     const int total = per_head * a.B * a.H;
-    int id = blockIdx.x;
+    int id = __builtin_amdgcn_workgroup_id_x();
     if ((total & 7) == 0) {
         const int per = total >> 3;
         id = (id & 7) * per + (id >> 3);
@@ -313,9 +324,12 @@ void fwd_fp8_kernel(Fp8Args a) {
     const int bh = id / per_head, p = id % per_head;
     const int hi = CAUSAL ? n_qt - 1 - p : p;
     const int n_tiles = (CAUSAL && p < hi) ? 2 : 1;
+    // The first tile's loads are issued and waited for at its start; the
+    // second tile's by the first one's end (the handover below), which also
+    // carries its Q block scale and first K/V block scales in these.
+    float sq_next = 1.f, ks_next = 1.f, vs_next = 1.f;
 #pragma nounroll
     for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
-        if (r) __syncthreads();           // every wave is done with the first tile's LDS
         const int qt = r ? p : hi;
         const int b = bh / a.H, h = bh % a.H;
         const int64_t npad = fp8_npad(a.N);
@@ -327,7 +341,7 @@ void fwd_fp8_kernel(Fp8Args a) {
         const int nqb = (a.N + kQBlk - 1) / kQBlk, nkb = (a.N + kKBlk - 1) / kKBlk;
         const int nvb = (a.N + kVBlk - 1) / kVBlk;
 
-        const int tid = threadIdx.x, lane = tid & 63;
+        const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int j = lane & 31, hh = lane >> 5;
         const int q0 = qt * BR + wave * WQ;
@@ -338,45 +352,89 @@ void fwd_fp8_kernel(Fp8Args a) {
         int wnt = CAUSAL ? min(nt, (min(a.N, q0 + WQ) + BC - 1) / BC) : nt;
         if (q0 >= a.N) wnt = 0;
 
-        // direct global -> LDS copies (1 KB per wave instruction, XOR-swizzled rows)
-        auto copy_k = [&](int kt, char* dst) {
+        // Outside the main loop, per-lane addresses start from an opaque copy
+        // of the lane index: computed once and shared with the other end of
+        // the tile they would stay live across the loop, be spilled, and
+        // their reloads would wait for every copy in flight.
+        auto fresh_lane = [&]() {
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            return l;
+        };
+        // direct global -> LDS copies (1 KB per wave instruction, XOR-swizzled
+        // rows); l is the lane index (or an opaque copy of it)
+        auto copy_k = [&](int kt, char* dst, int l) {
             for (int bk = wave; bk < NBK; bk += NW) {
-                const int c = bk * 64 + lane;
+                const int c = bk * 64 + l;
                 const int row = c / TL::KCPR, pch = c % TL::KCPR;
                 const int key = min(kt * BC + row, a.N - 1);
                 const uint8_t* g = Kg + int64_t(key) * D + 16 * (pch ^ TL::kswz(row));
                 copy16_to_lds(g, dst + bk * 1024);
             }
         };
-        auto copy_v = [&](int kt, char* dst) {
+        auto copy_v = [&](int kt, char* dst, int l) {
             for (int bk = wave; bk < NBV; bk += NW) {
-                const int c = bk * 64 + lane;
+                const int c = bk * 64 + l;
                 const int row = c / 4, pch = c % 4;  // row = head-dim index
                 const uint8_t* g = Vg + int64_t(row) * npad + int64_t(kt) * BC + 16 * (pch ^ TL::vswz(row));
                 copy16_to_lds(g, dst + bk * 1024);
             }
         };
 
+        // Q in and O out through the wave's own LDS slice, so that global
+        // memory sees whole rows (1 KB copies of Q; 16 bytes of an O row per
+        // lane) and only the registers hold the transposed layout.  A wave
+        // touches only its own slice: no workgroup barrier is involved.
+        char* const qo = lds_qo + wave * TL::SLICE;
+        constexpr int QCPR = D / 16;                     // 16-byte chunks per e4m3 row
+        constexpr int QBLK = 32 * D / 1024;               // 1 KB copies per plane
+        // rows past the end copy the last row (never stored)
+        auto copy_q = [&](int t) {
+            const int r0 = t * BR + wave * WQ, l = fresh_lane();
+    #pragma unroll
+            for (int pl = 0; pl < QTERMS; ++pl)
+    #pragma unroll
+                for (int i = 0; i < QBLK; ++i) {
+                    const int c = i * 64 + l, row = c / QCPR, pch = c % QCPR;
+                    const uint8_t* g = Qg + pl * q_plane + int64_t(min(r0 + row, a.N - 1)) * D + 16 * (pch ^ TL::qswz(row));
+                    copy16_to_lds(g, qo + pl * (32 * D) + i * 1024);
+                }
+        };
+        if (r == 0) {
+            copy_q(qt);
+            if (nt > 0) {
+                copy_k(0, lds_k0, lane);
+                copy_v(0, lds_v0, lane);
+            }
+            if (nt > 1) copy_k(1, lds_k1, lane);
+        }
+
         // Q^T operands: lane (query j, half hh) holds Q[qi][64ks + 32hh .. +31],
         // of the first e4m3 term (qhi) and of the residual term (qlo, which
         // the matrix core scales by 2^-4 through its E8M0 B-operand scale).
         i32x8 qhi[KS], qlo[KS];
+        auto read_q = [&]() {
+            const int l = fresh_lane(), jj = l & 31, h2 = l >> 5;
     #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 h0 = make_uint4(0, 0, 0, 0), h1 = h0, l0 = h0, l1 = h0;
-            if (qi < a.N) {
-                const uint8_t* p = Qg + int64_t(qi) * D + 64 * ks + 32 * hh;
-                h0 = *reinterpret_cast<const uint4*>(p);
-                h1 = *reinterpret_cast<const uint4*>(p + 16);
+            for (int ks = 0; ks < KS; ++ks) {
+                const char* rp = qo + jj * D;
+                const int c0 = (4 * ks + 2 * h2) ^ TL::qswz(jj), c1 = (4 * ks + 2 * h2 + 1) ^ TL::qswz(jj);
+                const uint4 h0 = *reinterpret_cast<const uint4*>(rp + 16 * c0);
+                const uint4 h1 = *reinterpret_cast<const uint4*>(rp + 16 * c1);
+                qhi[ks] = i32x8{int(h0.x), int(h0.y), int(h0.z), int(h0.w), int(h1.x), int(h1.y), int(h1.z), int(h1.w)};
+                uint4 l0 = make_uint4(0, 0, 0, 0), l1 = l0;
                 if (QTERMS == 2) {
-                    l0 = *reinterpret_cast<const uint4*>(p + q_plane);
-                    l1 = *reinterpret_cast<const uint4*>(p + q_plane + 16);
+                    l0 = *reinterpret_cast<const uint4*>(rp + 32 * D + 16 * c0);
+                    l1 = *reinterpret_cast<const uint4*>(rp + 32 * D + 16 * c1);
                 }
+                qlo[ks] = i32x8{int(l0.x), int(l0.y), int(l0.z), int(l0.w), int(l1.x), int(l1.y), int(l1.z), int(l1.w)};
             }
-            qhi[ks] = i32x8{int(h0.x), int(h0.y), int(h0.z), int(h0.w), int(h1.x), int(h1.y), int(h1.z), int(h1.w)};
-            qlo[ks] = i32x8{int(l0.x), int(l0.y), int(l0.z), int(l0.w), int(l1.x), int(l1.y), int(l1.z), int(l1.w)};
-        }
-        const float sq = (q0 < a.N) ? a.qs[int64_t(bh) * nqb + q0 / kQBlk] : 1.f;
+        };
+        auto qscale = [&](int t) {   // one value per wave: a wave-uniform index
+            const int w0 = t * BR + wave * WQ;
+            return (w0 < a.N) ? a.qs[__builtin_amdgcn_readfirstlane(bh * nqb + w0 / kQBlk)] : 1.f;
+        };
+        const float sq = r ? sq_next : qscale(qt);
         const float c2q = a.scale_log2 * sq;
 
         f32x16 oacc[DT];
@@ -503,29 +561,30 @@ void fwd_fp8_kernel(Fp8Args a) {
             lsum += rs[0];
         };
 
-        if (nt > 0) {
-            copy_k(0, lds_k0);
-            copy_v(0, lds_v0);
-        }
-        if (nt > 1) copy_k(1, lds_k1);
         // Block scales of the tile a step works on are loaded one step ahead,
         // before that step's tile copies: a wait for them is then never a wait
         // for the copies (loads retire in order).  Lane half hh holds the keys
         // of K block 2kt + hh.
-        auto kscale = [&](int kt) { return a.ks[int64_t(bh) * nkb + min(2 * kt + hh, nkb - 1)]; };
+        auto kscale = [&](int kt, int l) { return a.ks[int64_t(bh) * nkb + min(2 * kt + (l >> 5), nkb - 1)]; };
         auto vscale = [&](int kt) { return a.vs[int64_t(bh) * nvb + min(kt, nvb - 1)]; };
-        float ks_cur = kscale(0), vs_cur = vscale(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        float ks_cur = r ? ks_next : kscale(0, lane), vs_cur = r ? vs_next : vscale(0);
+        if (r == 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        read_q();
         f32x16 sA[2], sB[2];
         if (wnt > 0) scores(sA, lds_k0);
-        __syncthreads();
+        // every wave is done with K0 before K2 overwrites it (LDS reads only:
+        // the previous tile's O stores need not have completed)
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();
 
         auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], char* k_cur, char* k_nxt, char* v_cur,
                         char* v_nxt) {
-            const float ks_nxt = kscale(kt + 1), vs_nxt = vscale(kt + 1);
-            if (kt + 2 < nt) copy_k(kt + 2, k_cur);
-            if (kt + 1 < nt) copy_v(kt + 1, v_nxt);
+            const float ks_nxt = kscale(kt + 1, lane), vs_nxt = vscale(kt + 1);
+            if (kt + 2 < nt) copy_k(kt + 2, k_cur, lane);
+            if (kt + 1 < nt) copy_v(kt + 1, v_nxt, lane);
             if (kt < wnt) softmax_pv(cur, kt, ks_cur, vs_cur, v_cur, nxt, k_nxt);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -537,21 +596,59 @@ void fwd_fp8_kernel(Fp8Args a) {
             if (kt + 1 < nt) step(kt + 1, sB, sA, lds_k1, lds_k0, lds_v1, lds_v0);
         }
 
-        if (qi < a.N && wnt > 0) {
-            const float lt = lsum;   // the row sum already covers both lane halves
-            const float inv = 1.0f / lt;
-            uint16_t* orow = Og + int64_t(qi) * a.oss;
+        // Handover: the second tile's K/V copies and block scales go out
+        // before this tile's epilogue (the loop's last barrier came after
+        // every wave's last LDS read); its Q rows follow once this wave's O
+        // rows have left the slice.
+        const bool hand = r + 1 < n_tiles;
+        if (hand) {
+            const int nt2 = CAUSAL ? min(n_kt_all, (min(a.N, (p + 1) * BR) + BC - 1) / BC) : n_kt_all;
+            const int l = fresh_lane();
+            if (nt2 > 0) {
+                copy_k(0, lds_k0, l);
+                copy_v(0, lds_v0, l);
+            }
+            if (nt2 > 1) copy_k(1, lds_k1, l);
+            sq_next = qscale(p);
+            ks_next = kscale(0, l);
+            vs_next = a.vs[__builtin_amdgcn_readfirstlane(bh * nvb)];
+        }
+
+        // O = O^T / l into the slice (row j, chunk 4 dt + c4, half hh), then
+        // out as whole rows: lane L holds row ORPI i + L / OCPR, chunk L % OCPR.
+        const float lt = lsum;   // the row sum already covers both lane halves
+        const float inv = 1.0f / lt;
+        constexpr int OCPR = D / 8, ORPI = 64 / OCPR;
+        const int le = fresh_lane();
     #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
     #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    __bf16 o4[4];
+            for (int c4 = 0; c4 < 4; ++c4) {
+                __bf16 o4[4];
     #pragma unroll
-                    for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * r + t] * inv);
-                    *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, o4);
-                }
-            if (hh == 0)
-                a.lse[int64_t(bh) * a.N + qi] = (m_ref + __log2f(lt) - 6.f) * 0.69314718055994531f;
+                for (int t = 0; t < 4; ++t) o4[t] = static_cast<__bf16>(oacc[dt][4 * c4 + t] * inv);
+                const int jj = le & 31, h2 = le >> 5;
+                *reinterpret_cast<uint2*>(qo + jj * (2 * D) + 16 * ((4 * dt + c4) ^ TL::oswz(jj)) + 8 * h2) =
+                    __builtin_bit_cast(uint2, o4);
+            }
+        if (wnt > 0) {
+            uint16_t* const Ow = Og + int64_t(q0) * a.oss;
+    #pragma unroll
+            for (int i = 0; i < WQ / ORPI; ++i) {
+                const int row = ORPI * i + le / OCPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(qo + row * (2 * D) + 16 * (le % OCPR));
+                if (q0 + row < a.N)
+                    *reinterpret_cast<uint4*>(Ow + int64_t(row) * a.oss + 8 * ((le % OCPR) ^ TL::oswz(row))) = v;
+            }
+            const int qe = q0 + (le & 31);
+            if (qe < a.N && le < 32)
+                a.lse[int64_t(bh) * a.N + qe] = (m_ref + __log2f(lt) - 6.f) * 0.69314718055994531f;
+        }
+        if (hand) {
+            __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's O rows are out of its slice
+            copy_q(p);
+            __builtin_amdgcn_s_waitcnt(0);        // the second tile's copies and scales have landed
+            __builtin_amdgcn_s_barrier();         // ... in every wave
         }
     }
 }

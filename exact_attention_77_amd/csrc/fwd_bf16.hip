@@ -158,7 +158,7 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     const u16* Vg = static_cast<const u16*>(a.v) + base;
     u16* Og = static_cast<u16*>(a.o) + base;
 
-    const int tid = threadIdx.x;
+    const int tid = __builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int j = lane & 31, hh = lane >> 5;
@@ -553,7 +553,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int n_qt = (a.N + BR - 1) / BR;
     const int per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
     const int total = per_head * a.B * a.H;
-    int id = blockIdx.x;
+    int id = __builtin_amdgcn_workgroup_id_x();
     if ((total & 7) == 0) {
         const int per = total >> 3;
         id = (id & 7) * per + (id >> 3);
