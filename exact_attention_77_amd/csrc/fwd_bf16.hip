@@ -40,11 +40,18 @@
 //    consecutive keys of one head-dim column.
 //  * K is prefetched two tiles ahead and V one tile ahead (two LDS buffers
 //    each), one workgroup barrier per tile.
+//  * Q rows come in and O rows go out through each wave's own LDS slice, so
+//    that global memory sees whole rows; only the registers hold the
+//    transposed (one query per lane) layout.
 //  * workgroups are renumbered so that the tiles of one head run on one XCD
 //    (the hardware deals workgroup ids round-robin over the 8 XCDs), which
 //    keeps that head's K/V in the XCD's L2; under the causal mask a workgroup
 //    processes a heavy and a light query tile of one head (tiles T-1-p and
-//    p), so all workgroups carry equal work.
+//    p), so all workgroups carry equal work, and the light tile's loads are
+//    issued before the heavy tile's epilogue.
+//  * workgroup and lane ids come from the compiler builtins: with the IEEE
+//    mode bit off (see the build) the device library's id functions cannot
+//    be inlined and would become real calls.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <math.h>
