@@ -93,6 +93,17 @@ __device__ __forceinline__ short4_t lds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((__attribute__((address_space(3))) char*)(p)));
 }
 
+// XOR swizzle of a row of a wave's row slice (32 rows of D bf16): 16 lanes
+// reading one chunk of 16 rows hit distinct bank groups.
+template <int D>
+__device__ __forceinline__ int rswz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// s_waitcnt immediate that waits for LDS (and scalar memory) operations only:
+// vmcnt and expcnt at their maxima, lgkmcnt 0.
+constexpr int kLgkm0 = 0xC07F;
+
 __device__ __forceinline__ bf16x8 cat(short4_t lo, short4_t hi) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
@@ -125,6 +136,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char qtile0[QT_BYTES], qtile1[QT_BYTES];   // Q, 64 rows
     __shared__ __attribute__((aligned(1024))) char otile0[QT_BYTES], otile1[QT_BYTES];   // dO, 64 rows
     __shared__ __attribute__((aligned(16))) float stat0[2 * BQ], stat1[2 * BQ];          // LSE*log2e, -D
+    // each wave's K and V rows in, its dV and dK rows out (two 32-row slices)
+    constexpr int SL = 32 * D * 2;
+    __shared__ __attribute__((aligned(1024))) char kvsl[NWV * 2 * SL];
 
     const int BH = a.B * a.H;
     const int n_kt = (a.N + BK - 1) / BK;
@@ -134,7 +148,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int n_tiles = (CAUSAL && kp < lo_kt) ? 2 : 1;
 #pragma nounroll
     for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
-        if (r) __syncthreads();           // every wave is done with the first tile's LDS
         const int kt = r ? lo_kt : kp;
         const int b = bh / a.H, h = bh % a.H;
         const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
@@ -150,17 +163,33 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int k0 = kt * BK;
         const int kw0 = k0 + 32 * wave;               // first key of this wave
         const int key = kw0 + j;                      // this lane's key
-        const int key_c = min(key, a.N - 1);          // keys past the end re-read the last row
 
+        // K and V rows come in, dV and dK rows go out, through this wave's two
+        // LDS slices, so that global memory sees whole rows (1 KB copies in;
+        // 16 bytes of a row per lane out); only the registers hold the one-key-
+        // per-lane layout.  A wave touches only its own slices: no barrier.
+        // The slice addressing starts from an opaque copy of the lane index at
+        // each use, so that nothing of it stays live across the main loop.
+        char* const sk = kvsl + wave * 2 * SL;
+        char* const sv = sk + SL;
+        auto fresh_lane = [&]() {
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            return l;
+        };
+        auto copy_rows = [&](int kt_) {   // keys past the end copy the last row
+            const int l = fresh_lane(), r0 = kt_ * BK + 32 * wave;
+    #pragma unroll
+            for (int i = 0; i < SL / 1024; ++i) {
+                const int c = i * 64 + l, row = c / CPR, pch = c % CPR;
+                const int64_t off = int64_t(min(r0 + row, a.N - 1)) * a.ss + 8 * (pch ^ rswz<D>(row));
+                copy16_to_lds(Kg + off, sk + i * 1024);
+                copy16_to_lds(Vg + off, sv + i * 1024);
+            }
+        };
         // B operands of S = Q K^T and dP = dO V^T: lane (key, half hh), k-step
         // ks holds columns 16ks + 8hh .. +7 of the key's K and V rows
         bf16x8 kreg[KS], vreg[KS];
-    #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int64_t off = int64_t(key_c) * a.ss + 16 * ks + 8 * hh;
-            kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + off));
-            vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + off));
-        }
 
         auto copy_q = [&](int q0, auto bufc) {
             constexpr int buf = decltype(bufc)::value;
@@ -322,7 +351,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
             dvdk(2, [](int) {});
         };
 
-        if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
+        // The first tile's loads are issued here; the second tile's by the
+        // first one's end (below).
+        if (r == 0) {
+            copy_rows(kt);
+            if (qt0 < n_qt) copy_q(qt0 * BQ, std::integral_constant<int, 0>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's K and V rows have landed
+        {
+            const int l = fresh_lane(), jj = l & 31, h2 = l >> 5;
+    #pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = jj * (2 * D) + 16 * ((2 * ks + h2) ^ rswz<D>(jj));
+                kreg[ks] = *reinterpret_cast<const bf16x8*>(sk + off);
+                vreg[ks] = *reinterpret_cast<const bf16x8*>(sv + off);
+            }
+        }
         auto step = [&](int it, auto bufc) {
             constexpr int buf = decltype(bufc)::value;
             __builtin_amdgcn_s_waitcnt(0);
@@ -335,11 +379,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
             if (it + 1 < n_qt) step(it + 1, std::integral_constant<int, 1>{});
         }
 
-        // ---- epilogue: dV and dK = scale * (dK^T)^T, bf16 -------------------------
-        // register g of lane half hh: column 32dt + 8(g>>2) + 4hh + (g&3) of key `key`
-        if (key < a.N) {
-            u16* rv = static_cast<u16*>(a.dv) + base + int64_t(key) * a.ss;
-            u16* rk = static_cast<u16*>(a.dk) + base + int64_t(key) * a.ss;
+        // ---- handover: the second tile's first Q/dO tile goes out now --------
+        const bool hand = r + 1 < n_tiles;
+        if (hand) {
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_s_barrier();   // every wave is done with the Q/dO tiles
+            const int qt0n = CAUSAL ? (lo_kt * BK) / BQ : 0;
+            if (qt0n < n_qt) copy_q(qt0n * BQ, std::integral_constant<int, 0>{});
+        }
+
+        // ---- epilogue: dV and dK = scale * (dK^T)^T, bf16, via the slices ------
+        // register g of lane half hh: column 32dt + 8(g>>2) + 4hh + (g&3) of the
+        // lane's key, i.e. chunk 4dt + (g>>2), half hh of its row
+        const int le = fresh_lane();
+        {
+            const int jj = le & 31, h2 = le >> 5;
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
     #pragma unroll
@@ -350,9 +404,30 @@ void bwd_dkdv_kernel(BwdArgs a) {
                         v4[t] = static_cast<__bf16>(accv[dt][4 * rr + t]);
                         k4[t] = static_cast<__bf16>(acck[dt][4 * rr + t] * a.scale);
                     }
-                    *reinterpret_cast<uint2*>(rv + 32 * dt + 8 * rr + 4 * hh) = __builtin_bit_cast(uint2, v4);
-                    *reinterpret_cast<uint2*>(rk + 32 * dt + 8 * rr + 4 * hh) = __builtin_bit_cast(uint2, k4);
+                    const int off = jj * (2 * D) + 16 * ((4 * dt + rr) ^ rswz<D>(jj)) + 8 * h2;
+                    *reinterpret_cast<uint2*>(sv + off) = __builtin_bit_cast(uint2, v4);
+                    *reinterpret_cast<uint2*>(sk + off) = __builtin_bit_cast(uint2, k4);
                 }
+        }
+        {
+            constexpr int RPI = 64 / CPR;   // rows per 16-byte-per-lane access
+            u16* const dvw = static_cast<u16*>(a.dv) + base + int64_t(kw0) * a.ss;
+            u16* const dkw = static_cast<u16*>(a.dk) + base + int64_t(kw0) * a.ss;
+    #pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int row = RPI * i + le / CPR, pch = le % CPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(sv + row * (2 * D) + 16 * pch);
+                const uint4 k = *reinterpret_cast<const uint4*>(sk + row * (2 * D) + 16 * pch);
+                if (kw0 + row < a.N) {
+                    const int64_t off = int64_t(row) * a.ss + 8 * (pch ^ rswz<D>(row));
+                    *reinterpret_cast<uint4*>(dvw + off) = v;
+                    *reinterpret_cast<uint4*>(dkw + off) = k;
+                }
+            }
+        }
+        if (hand) {
+            __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's rows are out of its slices
+            copy_rows(lo_kt);
         }
     }
 }
@@ -384,9 +459,9 @@ void bwd_dq_kernel(BwdArgs a) {
     const int bh = id / per_head, p = id % per_head;
     const int hi = CAUSAL ? n_qt - 1 - p : p;
     const int n_tiles = (CAUSAL && p < hi) ? 2 : 1;
+    static_assert(NW * 32 * D * 2 <= 2 * TB, "dQ rows of all waves fit in one K/V buffer pair");
 #pragma nounroll
     for (int r = 0; r < n_tiles; ++r) {   // one copy of the tile code
-        if (r) __syncthreads();           // every wave is done with the first tile's LDS
         const int qt = r ? p : hi;
         const int b = bh / a.H, h = bh % a.H;
         const int64_t base = int64_t(b) * a.sb + int64_t(h) * a.sh;
@@ -563,7 +638,9 @@ void bwd_dq_kernel(BwdArgs a) {
             }
         };
 
-        if (nt > 0) copy_kv(0, std::integral_constant<int, 0>{});
+        // the first tile's first K/V tile; the second tile's is issued by the
+        // first one's end (below)
+        if (r == 0 && nt > 0) copy_kv(0, std::integral_constant<int, 0>{});
         auto step = [&](int kt, auto bufc) {
             constexpr int buf = decltype(bufc)::value;
             __builtin_amdgcn_s_waitcnt(0);
@@ -576,18 +653,45 @@ void bwd_dq_kernel(BwdArgs a) {
             if (kt + 1 < nt) step(kt + 1, std::integral_constant<int, 1>{});
         }
 
-        // ---- epilogue: dQ = scale * (dQ^T)^T, bf16 -------------------------------
-        if (qi < a.N) {
-            u16* row = static_cast<u16*>(a.dq) + base + int64_t(qi) * a.ss;
+        // ---- end of tile: every wave is done with the K/V buffers; the second
+        // tile's first K/V tile goes out at once (into buffer 0) ----------------
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();
+        if (r + 1 < n_tiles) {
+            const int nt2 = CAUSAL ? min(n_kt, (min(a.N, (p + 1) * BR) + BC - 1) / BC) : n_kt;
+            if (nt2 > 0) copy_kv(0, std::integral_constant<int, 0>{});
+        }
+
+        // ---- epilogue: dQ = scale * (dQ^T)^T, bf16, through buffer 1 ------------
+        // Wave w owns 32 rows of buffer 1 (waves 0-3 in the K half, 4-7 in the V
+        // half): dQ^T goes in as the lane's row (chunk 4dt + r4, half hh), the
+        // rows come out 16 bytes per lane, so that global memory sees whole rows.
+        // The next tile's first step copies into buffer 1 only after its
+        // barrier, which every wave reaches after reading its rows back.
+        {
+            constexpr int SL = 32 * D * 2, RPI = 64 / CPR;
+            char* const os = ((wave < NW / 2) ? ktile1 : vtile1) + (wave % (NW / 2)) * SL;
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            const int jj = le & 31, h2 = le >> 5;
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
     #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r4 = 0; r4 < 4; ++r4) {
                     __bf16 x4[4];
     #pragma unroll
-                    for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r + t] * a.scale);
-                    *reinterpret_cast<uint2*>(row + 32 * dt + 8 * r + 4 * hh) = __builtin_bit_cast(uint2, x4);
+                    for (int t = 0; t < 4; ++t) x4[t] = static_cast<__bf16>(acc[dt][4 * r4 + t] * a.scale);
+                    *reinterpret_cast<uint2*>(os + jj * (2 * D) + 16 * ((4 * dt + r4) ^ rswz<D>(jj)) + 8 * h2) =
+                        __builtin_bit_cast(uint2, x4);
                 }
+            u16* const dqw = static_cast<u16*>(a.dq) + base + int64_t(q0) * a.ss;
+    #pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int row = RPI * i + le / CPR, pch = le % CPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(os + row * (2 * D) + 16 * pch);
+                if (q0 + row < a.N)
+                    *reinterpret_cast<uint4*>(dqw + int64_t(row) * a.ss + 8 * (pch ^ rswz<D>(row))) = v;
+            }
         }
     }
 }
