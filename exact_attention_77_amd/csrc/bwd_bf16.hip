@@ -118,9 +118,9 @@ __device__ __forceinline__ bf16x8 cat(short4_t lo, short4_t hi) {
 // after exp2 and the bf16 conversion they are directly the B operands of
 // dV^T += dO^T P and dK^T += Q^T dS for the 16-query chunks 2qs + c' (A
 // operands dO^T, Q^T by transposing LDS reads).  Nothing goes back through
-// LDS, and each Q / dO row is read by the 4 waves of the workgroup instead of
-// 8.  The two 128-register accumulators leave room for the operands only at
-// one wave per SIMD.  The subtiles are pipelined so that the exp/dS work of
+// LDS, and each Q / dO row is read by the 4 waves of the workgroup.  The two
+// accumulators (128 registers together at d = 128, in the accumulation
+// registers) leave room for the operands only at one wave per SIMD.  The subtiles are pipelined so that the exp/dS work of
 // one sits beside the products of the other.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))

@@ -12,10 +12,14 @@
 //
 // gfx950 mapping:
 //  * pre-pass: one workgroup per (batch, head, row block); a row is spread over
-//    D/4 lanes (4 elements each); the fast Walsh-Hadamard transform does its
-//    two in-lane stages and log2(D/4) cross-lane stages with lane shuffles;
+//    D/32 lanes (32 elements each); the fast Walsh-Hadamard transform does its
+//    five in-lane stages and log2(D/32) cross-lane stages with DPP permutes;
 //    conversion uses v_cvt_pk_fp8_f32 (round to nearest even) on values clamped
-//    to +-448, which gives the saturating e4m3fn encoding.  V is written
+//    to +-448, which gives the saturating e4m3fn encoding.  Q also gets a
+//    second e4m3 term, 16 times its rounding residual (Q = scale (code +
+//    residual / 16)), which the attention kernel can add as a second score
+//    product.
+//    V is written
 //    transposed ([d][keys], padded to 64 keys) through an LDS tile, so the
 //    attention kernel's PV operand is a plain contiguous LDS read.
 //  * attention: like the bf16 kernel, a wave owns 32 queries and computes the
@@ -23,6 +27,9 @@
 //    (K = 64 fp8 per step).  K rows enter the product in an order that leaves,
 //    in lane half h, exactly keys 32h .. 32h+31 of the 64-key tile, so the
 //    packed fp8 probabilities are the B operand of O^T += V^T P^T directly.
+//    With both Q terms the score is the code product plus the residual
+//    product, whose E8M0 B-operand scale is 2^-4 (a second MFMA per k-step
+//    on the same K operand).
 //    Q and K block scales fold into the exp2 constant (the Q block is the
 //    wave's 32 rows, the K block the 32 keys a lane half holds, so both are
 //    per-lane scalars); the V block scale is a power of two handed to the

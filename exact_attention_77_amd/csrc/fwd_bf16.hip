@@ -29,8 +29,9 @@
 //    after exp2 and a bf16 conversion, already the B operand of the second
 //    product O^T += V^T P^T: no LDS round trip for P.
 //  * O^T stays in registers with one query per lane, so the rescale factor is
-//    a per-lane scalar; the row sum is accumulated from the bf16
-//    probabilities with v_dot2 (two per op), the same values that multiply V.
+//    a per-lane scalar; the row sum is taken on the matrix core (a product of
+//    a constant 0/1 operand with the bf16 probabilities), so it sums exactly
+//    the values that multiply V.
 //  * K and V tiles are copied global -> LDS by the direct-to-LDS loads of
 //    gfx950 (global_load_lds_dwordx4: no registers, no LDS store
 //    instructions), row-major and unpadded.  Each lane picks the 16-byte chunk
