@@ -108,7 +108,11 @@ def test_overlapping_rows_rejected(lay):
     fa.Layout(1, 4, 1, 128, 0, 128, 128),            # one row: its stride is irrelevant
     fa.Layout(3, 1, 7, 64, 7 * 64 + 64, 0, 64)])     # one head, padded batches
 def test_one_to_one_layouts_accepted(lay):
-    assert fwd(lay=lay, q=None) == 1   # passes every layout check, then reports the NULL q
+    # flash_attn_bwd checks the forward's layout rules before its workspace:
+    # without a workspace an accepted layout reports FLASH_ATTN_ERR_WORKSPACE
+    # (no kernel is launched)
+    assert fa.load().flash_attn_bwd(P, P, P, P, P, P, P, P, P, lay, fa.DTYPE_BF16, 0, 0.125,
+                                    None, 0, None) == 7
 
 
 def test_misaligned_pointers():
