@@ -23,6 +23,9 @@ flash_attn_status hip_status(int err) {
 constexpr int64_t kMaxRows = int64_t(1) << 24;
 constexpr int64_t kMaxTotalRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxMergeParts = 4096;
+// Row stride limit: the kernels address a tile's rows with 32-bit byte
+// offsets from the tile's first row (64 rows of at most 2^24 elements).
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,6 +56,7 @@ flash_attn_status check_shape(const flash_attn_layout& L) {
 flash_attn_status check_strides(const flash_attn_layout& L, int64_t elt_bytes) {
     const int64_t vec = 16 / elt_bytes;
     if (L.stride_s < L.head_dim || L.stride_h < 0 || L.stride_b < 0) return FLASH_ATTN_ERR_LAYOUT;
+    if (L.stride_s > kMaxRowStride) return FLASH_ATTN_ERR_LAYOUT;
     if (L.stride_s % vec || L.stride_h % vec || L.stride_b % vec) return FLASH_ATTN_ERR_LAYOUT;
     struct Dim { int64_t stride, extent; } dims[3] = {
         {L.stride_s, L.seqlen}, {L.stride_h, L.heads}, {L.stride_b, L.batch}};

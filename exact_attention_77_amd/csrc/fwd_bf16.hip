@@ -183,33 +183,68 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     // Wave w copies 1 KB blocks w*NI .. w*NI+NI-1 of the tile; lane L of a block
     // fills LDS chunk 64*blk + L, i.e. row (64*blk + L) / CPR, physical chunk
     // (64*blk + L) % CPR, which holds logical chunk (physical ^ swizzle(row)).
-    // The row a lane copies is the same in every tile, so its source pointer
-    // is fixed and a tile adds a wave-uniform offset.  In the ragged last tile
+    // The row a lane copies is the same in every tile, so its source address
+    // is fixed and a tile adds a wave-uniform offset.  At head_dim 128 a lane
+    // keeps a 32-bit byte offset per copy (the tile's first row is a
+    // wave-uniform base in scalar registers), which saves the registers that
+    // 64-bit addresses would hold (with four waves these spilled, and each
+    // reload waited for the copies in flight); at head_dim 64 the 64-bit
+    // addresses fit and measured slightly faster.  In the ragged last tile
     // rows past the end re-read the last row: their scores are masked to -inf,
     // so their probabilities are exactly 0.
-    int crow[NI];
-    const u16* kp[NI];
-    const u16* vp[NI];
+    constexpr bool OFF = D == 128;
+    constexpr int NA = OFF ? 1 : NI;  // 64-bit addresses kept per tensor
+    auto fresh_lane0 = [&]() {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    uint32_t koff[NI], voff[NI];   // OFF: byte offsets from the tile's first row
+    const u16* kp[NA];             // !OFF: the lane's source addresses in tile 0
+    const u16* vp[NA];
+    int crow[NA];                  // !OFF: the rows they copy
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int c = (wave * NI + i) * 64 + lane;
-        crow[i] = c / TL::CPR;
-        const int pch = c % TL::CPR;
-        kp[i] = Kg + int64_t(crow[i]) * a.ss + 8 * (pch ^ TL::kswz(crow[i]));
-        vp[i] = Vg + int64_t(crow[i]) * a.ss + 8 * (pch ^ TL::vswz(crow[i]));
+        const int row = c / TL::CPR, pch = c % TL::CPR;
+        if constexpr (OFF) {
+            koff[i] = 2u * uint32_t(row * a.ss + 8 * (pch ^ TL::kswz(row)));
+            voff[i] = 2u * uint32_t(row * a.ss + 8 * (pch ^ TL::vswz(row)));
+        } else {
+            crow[i] = row;
+            kp[i] = Kg + int64_t(row) * a.ss + 8 * (pch ^ TL::kswz(row));
+            vp[i] = Vg + int64_t(row) * a.ss + 8 * (pch ^ TL::vswz(row));
+        }
     }
-    auto copy_tile = [&](const u16* const (&src)[NI], int kt, int lds_off) {
+    auto copy_tile = [&](bool is_v, int kt, int lds_off) {
         const int k0 = kt * BC;
         if (k0 + BC <= a.N) {  // full tile: one wave-uniform offset
-            const int64_t off = int64_t(k0) * a.ss;
+            if constexpr (OFF) {
+                const u16* tb = (is_v ? Vg : Kg) + int64_t(k0) * a.ss;
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
-                copy16_to_lds(src[i] + off, smem + lds_off + (wave * NI + i) * 1024);
+                for (int i = 0; i < NI; ++i)
+                    copy16_to_lds_off(tb, is_v ? voff[i] : koff[i], smem + lds_off + (wave * NI + i) * 1024);
+            } else {
+                const int64_t off = int64_t(k0) * a.ss;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    copy16_to_lds((is_v ? vp[i] : kp[i]) + off, smem + lds_off + (wave * NI + i) * 1024);
+            }
+        } else if constexpr (OFF) {
+            const int l = fresh_lane0();
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int c = (wave * NI + i) * 64 + l;
+                const int row = c / TL::CPR, pch = c % TL::CPR;
+                const int sw = is_v ? TL::vswz(row) : TL::kswz(row);
+                copy16_to_lds((is_v ? Vg : Kg) + int64_t(min(k0 + row, a.N - 1)) * a.ss + 8 * (pch ^ sw),
+                              smem + lds_off + (wave * NI + i) * 1024);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int64_t row_off = int64_t(min(k0 + crow[i], a.N - 1) - crow[i]);
-                copy16_to_lds(src[i] + row_off * a.ss, smem + lds_off + (wave * NI + i) * 1024);
+                copy16_to_lds((is_v ? vp[i] : kp[i]) + row_off * a.ss, smem + lds_off + (wave * NI + i) * 1024);
             }
         }
     };
@@ -459,10 +494,10 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     // ---- prologue: Q^T, K0, V0, K1 in flight; S(0) -----------------------------
     auto first_copies = [&](int n) {
         if (n > 0) {
-            copy_tile(kp, 0, K_OFF0);
-            copy_tile(vp, 0, V_OFF0);
+            copy_tile(false, 0, K_OFF0);
+            copy_tile(true, 0, V_OFF0);
         }
-        if (n > 1) copy_tile(kp, 1, K_OFF1);
+        if (n > 1) copy_tile(false, 1, K_OFF1);
     };
     if (!issued) {
         copy_q(qt);
@@ -486,8 +521,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     // ---- main loop, unrolled by two so buffers and score sets alternate ------
     auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], int k_cur_off, int k_nxt_off,
                     int v_cur_off, int v_nxt_off) {
-        if (kt + 2 < nt) copy_tile(kp, kt + 2, k_cur_off);
-        if (kt + 1 < nt) copy_tile(vp, kt + 1, v_nxt_off);
+        if (kt + 2 < nt) copy_tile(false, kt + 2, k_cur_off);
+        if (kt + 1 < nt) copy_tile(true, kt + 1, v_nxt_off);
         if (kt < wnt) {
             main_block(cur, smem + v_cur_off, nxt, smem + k_nxt_off);
             if (needs_mask(kt + 1)) apply_mask(nxt, kt + 1);  // at most the diagonal and the ragged tile

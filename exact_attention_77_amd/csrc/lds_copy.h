@@ -21,6 +21,19 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) 
                  :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(src) : "memory", "m0");
 }
 
+// The same with the source split into a wave-uniform base (scalar registers)
+// and a 32-bit per-lane byte offset: one vector register per copy instead of
+// a 64-bit address.
+__device__ __forceinline__ void copy16_to_lds_off(const void* base, uint32_t off, const void* lds) {
+    typedef __attribute__((address_space(3))) const void lds_cvoid;
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)lds));
+    const uint64_t b = reinterpret_cast<uintptr_t>(base);
+    const uint64_t sb = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)))) |
+                        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)))) << 32);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off), "s"(sb) : "memory", "m0");
+}
+
 // The same for 4 bytes per lane (lane l fills lds + 4 l .. +3).
 __device__ __forceinline__ void copy4_to_lds(const void* src, const void* lds) {
     typedef __attribute__((address_space(3))) const void lds_cvoid;

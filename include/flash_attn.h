@@ -28,7 +28,9 @@
  *    base + b*stride_b + h*stride_h + i*stride_s + c (strides in elements, the
  *    head_dim stride is 1).  This expresses both [B, H, N, d] and [B, N, H, d].
  *    Base pointers must be 16-byte aligned and the strides multiples of
- *    16 bytes' worth of elements (8 for bf16, 4 for f32, 16 for fp8).
+ *    16 bytes' worth of elements (8 for bf16, 4 for f32, 16 for fp8);
+ *    stride_s is at most 2^24 elements (rows of a tile are addressed with
+ *    32-bit offsets).
  *  - LSE is always a contiguous fp32 [B, H, N] array.
  *  - Inputs must be finite.  A NaN or infinite element of Q, K or V leaves the
  *    outputs of the rows that use it (and possibly of other rows whose key

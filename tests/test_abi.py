@@ -83,9 +83,17 @@ def test_unsupported_head_dim(d):
     assert fwd(lay=_lay(d=d)) == 5
 
 
-@pytest.mark.parametrize("lay", [_lay(ss=60), _lay(ss=68), _lay(sh=8), _lay(sb=4, H=1, B=2)])
+@pytest.mark.parametrize("lay", [_lay(ss=60), _lay(ss=68), _lay(sh=8), _lay(sb=4, H=1, B=2),
+                                 _lay(N=2, ss=(1 << 24) + 8)])   # row stride beyond 2^24 elements
 def test_bad_strides(lay):
     assert fwd(lay=lay) == 3
+
+
+def test_row_stride_limit():
+    # 2^24 elements is accepted (the backward's workspace check comes next)
+    lay = _lay(N=2, ss=1 << 24)
+    assert fa.load().flash_attn_bwd(P, P, P, P, P, P, P, P, P, lay, fa.DTYPE_BF16, 0, 0.125,
+                                    None, 0, None) == 7
 
 
 @pytest.mark.parametrize("lay", [

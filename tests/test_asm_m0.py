@@ -8,7 +8,8 @@ in M0 across the copy would be corrupted.  The kernels are therefore correct
 only while the compiler itself never uses M0 in them.  This test compiles
 every kernel source that includes the helper to assembly, with the library's
 own flags, and fails if any instruction outside the helper's inline-assembly
-blocks names M0, or if a block differs from the helper's three instructions.
+blocks names M0, or if a block differs from the helper's three instructions (the copy takes
+a 64-bit address, or a 32-bit offset from a base in scalar registers).
 """
 import os
 import re
@@ -20,7 +21,8 @@ import pytest
 
 from exact_attention_77_amd import build as B
 
-HELPER_BLOCK = [r"s_mov_b32 m0, s\d+", r"s_nop 0", r"global_load_lds_dword(x4)? v\[\d+:\d+\], off"]
+HELPER_BLOCK = [r"s_mov_b32 m0, s\d+", r"s_nop 0",
+                r"global_load_lds_dword(x4)? (v\[\d+:\d+\], off|v\d+, s\[\d+:\d+\])"]
 
 
 def _sources_using_helper():
