@@ -21,9 +21,11 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) 
                  :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(src) : "memory", "m0");
 }
 
-// The same with the source split into a wave-uniform base (scalar registers)
-// and a 32-bit per-lane byte offset: one vector register per copy instead of
-// a 64-bit address.
+// The same with the source split into a base and a 32-bit per-lane byte
+// offset (the address is base + off, the offset zero-extended): one vector
+// register per copy instead of a 64-bit address.  `base` must be the same in
+// every lane of the wave; it is read from the first active lane into scalar
+// registers (a no-op when the compiler already holds it there).
 __device__ __forceinline__ void copy16_to_lds_off(const void* base, uint32_t off, const void* lds) {
     typedef __attribute__((address_space(3))) const void lds_cvoid;
     const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)lds));
