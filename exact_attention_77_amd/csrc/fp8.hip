@@ -543,15 +543,34 @@ void fwd_fp8_kernel(Fp8Args a) {
                 pb[r4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
             };
             constexpr int CPM = 8 / NQK;   // probability chunks per score product
-            i32x8 kop[2];
+            // The next k-step's K operands are read two products before they
+            // are needed (+1 %), except in the causal two-term kernel, whose
+            // registers do not have room for them (it spilled: -7 %).
+            constexpr bool KRA = !(CAUSAL && QTERMS == 2);
+            constexpr int QPK = QTERMS == 2 ? 4 : 2;   // score products per k-step
+            i32x8 kop[2], kn[2];
+            if (KRA) {
+                kop[0] = k_operand(knext, 0, 0);
+                kop[1] = k_operand(knext, 1, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
             for (int q = 0; q < NQK; ++q) {
-                if ((q & (QTERMS == 2 ? 3 : 1)) == 0) {
-                    kop[0] = k_operand(knext, 0, q >> (QTERMS == 2 ? 2 : 1));
-                    kop[1] = k_operand(knext, 1, q >> (QTERMS == 2 ? 2 : 1));
+                const int ks = q / QPK, pos = q % QPK;
+                if (KRA) {
+                    if (pos == QPK - 2 && ks + 1 < KS) {
+                        kn[0] = k_operand(knext, 0, ks + 1);
+                        kn[1] = k_operand(knext, 1, ks + 1);
+                    }
+                } else if (pos == 0) {
+                    kop[0] = k_operand(knext, 0, ks);
+                    kop[1] = k_operand(knext, 1, ks);
                 }
                 score_mfma(nxt, kop, q);
+                if (KRA && pos == QPK - 1 && ks + 1 < KS) {
+                    kop[0] = kn[0];
+                    kop[1] = kn[1];
+                }
     #pragma unroll
                 for (int c = 0; c < CPM; ++c) exp_chunk(q * CPM + c);
                 __builtin_amdgcn_sched_barrier(0);
