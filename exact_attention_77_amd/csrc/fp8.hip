@@ -544,11 +544,12 @@ void fwd_fp8_kernel(Fp8Args a) {
             };
             constexpr int CPM = 8 / NQK;   // probability chunks per score product
             // The next k-step's K operands are read two products before they
-            // are needed (+1 %), except in the causal two-term kernel, whose
-            // registers do not have room for them (it spilled: -7 %).
+            // are needed (+1 %), and the first V^T operand during the last two
+            // score products (+0.5 %), except in the causal two-term kernel,
+            // whose registers do not have room for them (it spilled: -7 %).
             constexpr bool KRA = !(CAUSAL && QTERMS == 2);
             constexpr int QPK = QTERMS == 2 ? 4 : 2;   // score products per k-step
-            i32x8 kop[2], kn[2];
+            i32x8 kop[2], kn[2], va0;
             if (KRA) {
                 kop[0] = k_operand(knext, 0, 0);
                 kop[1] = k_operand(knext, 1, 0);
@@ -566,6 +567,7 @@ void fwd_fp8_kernel(Fp8Args a) {
                     kop[0] = k_operand(knext, 0, ks);
                     kop[1] = k_operand(knext, 1, ks);
                 }
+                if (KRA && q == NQK - 2) va0 = v_operand(vt_lds, 0);   // the first PV operand
                 score_mfma(nxt, kop, q);
                 if (KRA && pos == QPK - 1 && ks + 1 < KS) {
                     kop[0] = kn[0];
@@ -577,7 +579,7 @@ void fwd_fp8_kernel(Fp8Args a) {
             }
             const f32x4 rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 ones_a, pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            i32x8 va = v_operand(vt_lds, 0);
+            i32x8 va = KRA ? va0 : v_operand(vt_lds, 0);
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const i32x8 vcur = va;

@@ -417,7 +417,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
     //           each paired with probabilities of the current tile
     //           (fma, exp2, bf16 pack, and the row-sum product of each
     //           completed chunk); then the check above;
-    //  phase 2: PV MFMAs of the current tile (V^T operands read NPV ahead).
+    //  phase 2: PV MFMAs of the current tile (V^T operands read NPV ahead;
+    //           the first NPV during the last score products).
     // On a wave's last tile the score product reads a valid but unused buffer.
     constexpr int QKM = 2 * KSTEPS;   // score MFMAs per tile
     constexpr int PVM = 4 * DT;       // PV MFMAs per tile
@@ -452,10 +453,15 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
         const f32x16 zero = {};
         flush_deferred();
         __builtin_amdgcn_sched_barrier(0);
+        bf16x8 vb[NPV];
 #pragma unroll
         for (int m = 0; m < QKM; ++m) {
             const bf16x8 ka = kb[m % NPK];
             if (m + NPK < QKM) kb[m % NPK] = k_operand(knext, m + NPK);
+            if (m == QKM - 2) {   // the first PV operands, in flight during the check
+#pragma unroll
+                for (int i = 0; i < NPV; ++i) vb[i] = v_operand(vt_lds, i);
+            }
             nxt[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[m >> 1], (m < 2) ? zero : nxt[m & 1], 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < PPM; ++q) {
@@ -477,9 +483,6 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, char* smem, int 
             lp = kRowsumMfma ? rs[0] : lpart[0] + lpart[1];
         }
         lsum += lp;
-        bf16x8 vb[NPV];
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) vb[i] = v_operand(vt_lds, i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < PVM - NDEF; ++n) {
