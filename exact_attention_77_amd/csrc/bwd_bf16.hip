@@ -256,8 +256,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
             const float* ls = buf ? stat1 : stat0;
             const int q0 = it * BQ;
             // S and dP - D of subtile qs: 2*KS products alternating, LDS
-            // operands read two ahead; `beside(m)` is issued after product m
-            auto sdp = [&](int qs, f32x16& sc, f32x16& dp, auto&& beside) {
+            // operands read two ahead (the first two, `pre`, during the
+            // previous phase: `prefetch()` reads the next phase's two beside
+            // this phase's second-last product); `beside(m)` is issued after
+            // product m
+            auto sdp_src = [&](int qs, int m) { return ld16((m & 1) ? ot : qt, 32 * qs * 2 * D + qo[m >> 1]); };
+            auto sdp = [&](int qs, f32x16& sc, f32x16& dp, const bf16x8 (&pre)[2], auto&& beside, auto&& prefetch) {
     #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const float4 nd = *reinterpret_cast<const float4*>(ls + BQ + 32 * qs + 16 * (rr >> 1) + 8 * hh + 4 * (rr & 1));
@@ -265,14 +269,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 }
     #pragma unroll
                 for (int g = 0; g < 16; ++g) sc[g] = 0.f;
-                auto src = [&](int m) { return ld16((m & 1) ? ot : qt, 32 * qs * 2 * D + qo[m >> 1]); };
+                auto src = [&](int m) { return sdp_src(qs, m); };
                 bf16x8 op[3];
-                op[0] = src(0);
-                op[1] = src(1);
+                op[0] = pre[0];
+                op[1] = pre[1];
                 __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
                 for (int m = 0; m < 2 * KS; ++m) {
                     if (m + 2 < 2 * KS) op[(m + 2) % 3] = src(m + 2);
+                    if (m == 2 * KS - 2) prefetch();
                     if (m & 1)
                         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m % 3], vreg[m >> 1], dp, 0, 0, 0);
                     else
@@ -318,19 +323,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
             };
             // dV^T and dK^T products of 16-query chunks c0, c0 + 1 (subtile
             // c0 / 2): 4*DT products, A operands read two ahead
-            auto dvdk = [&](int c0, auto&& beside) {
+            auto dvdk_src = [&](int c0, int n) {   // n: chunk c0 + (n / (2 DT)), tile dt, dO^T or Q^T
+                const int c = c0 + n / (2 * DT), dt = (n >> 1) % DT;
+                return ldtr((n & 1) ? qt : ot, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
+            };
+            auto dvdk = [&](int c0, const bf16x8 (&pre)[2], auto&& beside, auto&& prefetch) {
                 constexpr int NP = 4 * DT;
-                auto asrc = [&](int n) {   // n: chunk c0 + (n / (2 DT)), tile dt, dO^T or Q^T
-                    const int c = c0 + n / (2 * DT), dt = (n >> 1) % DT;
-                    return ldtr((n & 1) ? qt : ot, 32 * D * c + tro[dt][0], 32 * D * c + tro[dt][1]);
-                };
+                auto asrc = [&](int n) { return dvdk_src(c0, n); };
                 bf16x8 op[3];
-                op[0] = asrc(0);
-                op[1] = asrc(1);
+                op[0] = pre[0];
+                op[1] = pre[1];
                 __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
                 for (int n = 0; n < NP; ++n) {
                     if (n + 2 < NP) op[(n + 2) % 3] = asrc(n + 2);
+                    if (n == NP - 2) prefetch();
                     const int c = c0 + n / (2 * DT), dt = (n >> 1) % DT;
                     if (n & 1)
                         acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n % 3], dsb[c >> 1][c & 1], acck[dt], 0, 0, 0);
@@ -341,14 +348,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 }
             };
             f32x16 s0, dp0, s1, dp1;
-            sdp(0, s0, dp0, [](int) {});
+            bf16x8 preA[2], preB[2];
+            preA[0] = sdp_src(0, 0);
+            preA[1] = sdp_src(0, 1);
+            sdp(0, s0, dp0, preA, [](int) {}, [&]() { preB[0] = sdp_src(1, 0); preB[1] = sdp_src(1, 1); });
             mask(0, s0);
             constexpr int G1 = 16 / (2 * KS);   // subtile-0 registers beside each S/dP product of subtile 1
-            sdp(1, s1, dp1, [&](int m) { softmax(0, s0, dp0, G1 * m, G1 * (m + 1)); });
+            sdp(1, s1, dp1, preB, [&](int m) { softmax(0, s0, dp0, G1 * m, G1 * (m + 1)); },
+                [&]() { preA[0] = dvdk_src(0, 0); preA[1] = dvdk_src(0, 1); });
             mask(1, s1);
             constexpr int G2 = 16 / (4 * DT);   // subtile-1 registers beside each dV/dK product of subtile 0
-            dvdk(0, [&](int n) { softmax(1, s1, dp1, G2 * n, G2 * (n + 1)); });
-            dvdk(2, [](int) {});
+            dvdk(0, preA, [&](int n) { softmax(1, s1, dp1, G2 * n, G2 * (n + 1)); },
+                 [&]() { preB[0] = dvdk_src(2, 0); preB[1] = dvdk_src(2, 1); });
+            dvdk(2, preB, [](int) {}, []() {});
         };
 
         // The first tile's loads are issued here; the second tile's by the
