@@ -27,9 +27,10 @@
 //              B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by
 //              transposing LDS reads) -- no exchange through LDS.
 //  dQ kernel: one workgroup per (batch, head, 256-query tile), eight waves of
-//            32 queries, K/V tiles of 64 keys streamed through LDS (the loop
-//            order of the forward pass); each query row belongs to exactly one
-//            lane pair, which forms D_i from the row's dO (already in its
+//            32 queries, K/V tiles of 128 keys (worked in 64-key blocks)
+//            streamed through LDS (the loop order of the forward pass); each
+//            query row belongs to exactly one lane pair, which forms D_i from
+//            the row's dO (already in its
 //            registers) and O.  Per tile the transposed products
 //            S^T = K Q^T and dP^T - D = V dO^T (Q^T, dO^T held in registers)
 //            put one query per lane, dS^T = P^T (dP^T - D) -> bf16 is, with K
